@@ -1,0 +1,173 @@
+"""Throughput of the hot path on one MI355X.
+
+One step = one pass of every hot-path operation over resident synthetic
+inputs, enqueued on torch's current stream:
+  1. tla_gemm_epilogue   bf16 4096^3, D = ReLU(1.5*A.B + 0.5*C + bias), fp32 acc
+  2. tla_tiled_transpose fp32 16384 x 16384, row-major -> column-major
+  3. tla_thread_map_eval the 64x64 / 128-thread / width-4 / 8-iteration map
+
+Prints ONE JSON line.  `value` is the GEMM's TFLOP/s (2*M*N*K useful flops
+per launch over its average launch time, measured with HIP events recorded
+on the launch stream); the transpose's GB/s (algorithmic bytes: one read and
+one write of the matrix) is reported beside it, each with its roofline.
+`cpu_baseline` times the oracle on a bounded row sample of the same GEMM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "bf16 GEMM+epilogue TFLOP/s @4096³ (% MFMA peak); transpose GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(case, inp, target_s):
+    """The oracle (unchanged) on the first R rows of the GEMM: R is grown
+    until one run takes about target_s seconds; returns its TFLOP/s."""
+    from oracle import gemm as og
+    threads = min(og.host_threads(), 16)
+    rows = 4
+    while True:
+        kw = dict(M=rows, N=case.N, K=case.K, A=inp["A"][: rows * case.lda], a_type=case.a_type,
+                  a_order=case.a_order, lda=case.lda, B=inp["B"], b_type=case.b_type,
+                  b_order=case.b_order, ldb=case.ldb,
+                  C=inp["C"][: rows * case.ldc], c_type=case.c_type, c_order=case.c_order,
+                  ldc=case.ldc, bias=inp["bias"], bias_type=case.bias_type, alpha=case.alpha,
+                  beta=case.beta, act=case.act, nthreads=threads)
+        t0 = time.perf_counter()
+        og.gemm(**kw)
+        dt = time.perf_counter() - t0
+        if dt >= target_s * 0.5 or rows >= case.M:
+            break
+        rows = min(case.M, max(rows * 2, int(rows * target_s / max(dt, 1e-3))))
+    flops = 2.0 * rows * case.N * case.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d of %d output rows of the bf16 4096^3 GEMM+epilogue (all %d "
+                      "columns, full K); %.1f s" % (rows, case.M, case.N, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_layout_algebra_amd as tla
+    import workloads as W
+    from tests.gpu_util import to_dev
+
+    torch.cuda.set_device(0)
+    g = W.GEMM_BF16_4096
+    tc = W.TRANSPOSE_F32_16384
+    tmc = W.THREAD_MAP_64x64
+    inp = W.gemm_inputs(g)
+    dA, dB, dC, dbias = (to_dev(inp[k]) for k in ("A", "B", "C", "bias"))
+    dD = torch.empty(g.M * g.ldd, dtype=torch.int16, device="cuda")
+    tsrc = to_dev(W.transpose_input(tc))
+    tdst = torch.empty_like(tsrc)
+    n_map = tmc.T * tmc.V * tmc.I
+    midx = torch.empty(n_map, dtype=torch.int64, device="cuda")
+    mval = torch.empty(n_map, dtype=torch.uint8, device="cuda")
+    variant = tla.gemm_variant(g.M, g.N, g.K, dA, g.a_type, g.a_order, g.lda, dB, g.b_type,
+                               g.b_order, g.ldb, dD, g.d_type, g.d_order, g.ldd, C=dC,
+                               c_type=g.c_type, ldc=g.ldc, bias=dbias, bias_type=g.bias_type,
+                               alpha=g.alpha, beta=g.beta, act=g.act)
+    stream = torch.cuda.current_stream()
+
+    def gemm():
+        tla.gemm_epilogue(g.M, g.N, g.K, dA, g.a_type, g.a_order, g.lda, dB, g.b_type, g.b_order,
+                          g.ldb, dD, g.d_type, g.d_order, g.ldd, C=dC, c_type=g.c_type,
+                          c_order=g.c_order, ldc=g.ldc, bias=dbias, bias_type=g.bias_type,
+                          alpha=g.alpha, beta=g.beta, act=g.act, stream=stream.cuda_stream)
+
+    def transpose():
+        tla.tiled_transpose(tsrc, tc.ld_src, tdst, tc.ld_dst, tc.M, tc.N, 4,
+                            stream=stream.cuda_stream)
+
+    def tmap():
+        tla.thread_map_eval(tmc.R, tmc.C, tmc.T, tmc.V, tmc.I, tmc.contiguous_dim, tmc.R - 1,
+                            tmc.C, midx, mval, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        gemm(); transpose(); tmap()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        ev[s][0].record(stream)
+        gemm()
+        ev[s][1].record(stream)
+        transpose()
+        ev[s][2].record(stream)
+        tmap()
+        ev[s][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_gemm = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(K)]) * 1e-3
+    t_tr = np.array([ev[s][1].elapsed_time(ev[s][2]) for s in range(K)]) * 1e-3
+    gemm_tflops = g.flops() / t_gemm.mean() / 1e12
+    tr_gbs = tc.bytes_moved() / t_tr.mean() / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(gemm_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s + %s + %s" % (g.name, tc.name, tmc.name),
+                   "gemm": {"M": g.M, "N": g.N, "K": g.K, "a": "bf16 row-major",
+                            "b": "bf16 column-major", "c": "bf16 row-major", "bias": "bf16[N]",
+                            "alpha": g.alpha, "beta": g.beta, "act": "relu", "seed": g.seed,
+                            "variant": variant},
+                   "transpose": {"M": tc.M, "N": tc.N, "elem_bytes": 4, "seed": tc.seed}},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel_us": round(t_gemm.mean() * 1e6, 2),
+                     "kernel_us_min": round(t_gemm.min() * 1e6, 2)},
+        "transpose": {"value": round(tr_gbs, 1), "unit": "GB/s",
+                      "roofline": {"bound": "hbm", "achieved": round(tr_gbs, 1),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(tr_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                   "kernel_us": round(t_tr.mean() * 1e6, 2),
+                                   "kernel_us_min": round(t_tr.min() * 1e6, 2)}},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(g, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * tla.h -- C ABI of libtla.so: a layout-algebra-driven tiled GEMM with a
+ * fused epilogue, a layout-driven tiled transpose, and a device evaluator
+ * of shape/stride layouts, for AMD Instinct MI355X (gfx950 / CDNA4).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Plain C types only.  Device pointers are raw HIP device addresses;
+ *   `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ * - Ownership: the caller owns every buffer.  The library never allocates,
+ *   frees or retains user memory, keeps no global state and needs no
+ *   workspace, so it is reentrant.
+ * - Asynchrony: device work is enqueued on `stream` and the call returns.
+ *   Argument errors are reported synchronously (no work is enqueued);
+ *   execution faults surface at the caller's next synchronisation.
+ * - Status codes: TLA_OK (0) or a negative TLA_ERR_* value; no exceptions
+ *   cross the boundary.  tla_status_string() names them.
+ * - Sizes, leading dimensions and strides are counted in ELEMENTS.
+ *
+ * Sources of the operations (page titles and sections):
+ * - "CUTLASS / CuTe 主线" (hpc.payai.win/cutlass): section 一 maps
+ *   C[M,N] = A[M,K] x B[K,N] onto block / warp / instruction tiles and
+ *   ends in an epilogue (alpha/beta, bias/activation, store); section 二
+ *   describes the host entry as close to cuBLAS; section 三's Collective
+ *   Epilogue fuses scale/bias/activation; lesson 7 of its course table is
+ *   mixed precision with an fp32 accumulator.
+ * - "什么是 CuTe ?" (GPU Glossary zh, 4.21): the transpose of a row-major
+ *   tensor into a column-major one over the same shape, by tiles.
+ * - "Advanced CUTLASS Architecture and Kernel Optimization" (oboe.com),
+ *   "The Algebra of Layouts", "Functional Composition", "Advanced Layout
+ *   Operations": Layout = (Shape, Stride), crd2idx, composition,
+ *   logical_divide.
+ * - PitchLinearStripminedThreadMap walk-through (lpnh.cn/news/2469163),
+ *   sections 2.1, 3.1-3.4, 4.2: the strip-mined thread map, its tile
+ *   equation and its predicate; section 6.3: the pitch comes from the
+ *   tensor layout.
+ */
+#ifndef TLA_H
+#define TLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------- status */
+enum {
+  TLA_OK = 0,
+  TLA_ERR_INVALID_ARG = -1, /* NULL pointer, negative size, ld too small,
+                               C == NULL with beta != 0, n != domain size,
+                               tile equation violated, ...            */
+  TLA_ERR_UNSUPPORTED = -2, /* dtype / order combination not provided */
+  TLA_ERR_OVERLAP = -3,     /* transpose source and destination overlap */
+  TLA_ERR_HIP = -4          /* kernel launch failed (hipGetLastError is
+                               consumed by the call)                   */
+};
+
+/* ------------------------------------------------------- element types */
+typedef enum {
+  TLA_F16 = 0,  /* IEEE binary16                                        */
+  TLA_BF16 = 1, /* bfloat16                                             */
+  TLA_E4M3 = 2, /* OCP FP8 E4M3FN (bias 7, max 448, no inf)             */
+  TLA_F32 = 3   /* IEEE binary32 (bias / C only)                        */
+} tla_dtype;
+
+typedef enum { TLA_ROW_MAJOR = 0, TLA_COL_MAJOR = 1 } tla_order;
+
+typedef enum {
+  TLA_ACT_NONE = 0,
+  TLA_ACT_RELU = 1, /* max(y, 0)                                        */
+  TLA_ACT_GELU = 2  /* y * Phi(y), the erf form                         */
+} tla_act;
+
+/* -------------------------------------------------------------- GEMM */
+/*
+ * D = act( alpha*scale_a*scale_b * (A . B)  +  beta*C  +  bias )
+ *
+ * Logical shapes: A is M x K, B is K x N, C and D are M x N; bias has N
+ * entries (one per output column) or is NULL.  Each matrix has its own
+ * storage order and leading dimension: element (r, c) of a row-major
+ * matrix is at r*ld + c, of a column-major one at r + c*ld; ld must be at
+ * least the contiguous extent (and >= 1).
+ *
+ * Arithmetic: products of the A/B storage values are accumulated in fp32;
+ * the epilogue runs in fp32 (alpha_eff = alpha*scale_a*scale_b, then
+ * + beta*C(m,n) when beta != 0, + bias[n] when bias != NULL, then act) and
+ * rounds to D's type to nearest even.  C is not read when beta == 0 (it may
+ * then be NULL).  scale_a / scale_b are the per-tensor dequantisation
+ * scales of fp8 operands (pass 1 otherwise).
+ *
+ * Supported combinations:
+ *   A, B:  both F16, both BF16, or both E4M3
+ *   D:     F16 or BF16;  C and bias: F16, BF16 or F32
+ *   any order for A, B, C, D; any leading dimension; any alignment
+ *   (aligned, K-contiguous operands take the fast path, the rest a general
+ *   predicated path with the same results up to fp32 summation order).
+ *
+ * Edge cases: M == 0 or N == 0 is a no-op returning TLA_OK; K == 0 gives
+ * D = act(beta*C + bias).  D may alias C only with identical order and
+ * leading dimension.  Elements of D's padding (ld beyond the extent) are
+ * never written; elements of A, B, C padding are never read.
+ */
+typedef struct {
+  int64_t M, N, K;
+  const void *A; int32_t a_type; int32_t a_order; int64_t lda;
+  const void *B; int32_t b_type; int32_t b_order; int64_t ldb;
+  const void *C; int32_t c_type; int32_t c_order; int64_t ldc;
+  void *D;       int32_t d_type; int32_t d_order; int64_t ldd;
+  const void *bias; int32_t bias_type;
+  int32_t act;   /* tla_act */
+  float alpha, beta, scale_a, scale_b;
+} tla_gemm_args;
+
+int tla_gemm_epilogue(const tla_gemm_args *args, void *stream);
+
+/* Name of the kernel variant tla_gemm_epilogue would launch for `args`
+ * (written NUL-terminated into buf, at most cap bytes).  Host only. */
+int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
+
+/* --------------------------------------------------------- transpose */
+/*
+ * dst(m, n) = src(m, n) bit for bit, from a row-major source to a
+ * column-major destination over the same M x N shape:
+ *     dst[m + n*ld_dst] = src[m*ld_src + n]      (element units)
+ * elem_bytes: 1, 2, 4, 8 or 16; ld_src >= N, ld_dst >= M.  Elements are
+ * moved as raw bits (NaN payloads and subnormals are preserved).  The
+ * source and destination byte ranges must not overlap (TLA_ERR_OVERLAP).
+ * M == 0 or N == 0 is a no-op.  Destination padding is never written.
+ */
+int tla_tiled_transpose(const void *src, int64_t ld_src, void *dst, int64_t ld_dst,
+                        int64_t M, int64_t N, int32_t elem_bytes, void *stream);
+
+/* ---------------------------------------------------------- layouts */
+/*
+ * A shape/stride layout with at most one level of nesting: n_modes
+ * top-level modes, mode i made of leaves[i] leaves (1 = a plain integer
+ * mode); shape[] and stride[] list the leaf extents and strides mode by
+ * mode.  A 1-D index walks the layout colexicographically (first leaf
+ * fastest), and the value is the dot product of the leaf coordinates with
+ * the strides.  Extents must be >= 1.
+ *
+ * Example: the SM80 A-operand TV layout ((4,8),(2,2,2)):((32,1),(16,8,128))
+ * is n_modes 2, leaves {2,3}, shape {4,8,2,2,2}, stride {32,1,16,8,128}.
+ */
+#define TLA_MAX_MODES 8
+#define TLA_MAX_LEAVES 16
+typedef struct {
+  int32_t n_modes;
+  int32_t leaves[TLA_MAX_MODES];
+  int64_t shape[TLA_MAX_LEAVES];
+  int64_t stride[TLA_MAX_LEAVES];
+} tla_layout;
+
+/* Number of coordinates (product of all leaf extents).  Host only. */
+int tla_layout_size(const tla_layout *L, int64_t *size);
+
+/*
+ * out[i] = outer(i)             for i < n, when inner == NULL (n == size(outer))
+ * out[i] = outer(inner(i))      for i < n, otherwise       (n == size(inner))
+ * Composition is pointwise: inner's value is a 1-D index into outer's
+ * domain, so every inner(i) must lie in [0, size(outer)) -- checked on the
+ * host from the range of inner.  `out` is a device array of n int64.
+ */
+int tla_layout_eval(const tla_layout *outer, const tla_layout *inner, int64_t *out,
+                    int64_t n, void *stream);
+
+/*
+ * logical_divide of a flat layout (every mode one leaf) by a tile shape:
+ * mode i of extent n_i and stride d_i becomes the nested mode
+ * (tile_i, ceil(n_i/tile_i)) : (d_i, d_i*tile_i) -- position inside the
+ * tile first, tile index second.  n_tile == n_modes.  Host only.
+ */
+int tla_logical_divide(const tla_layout *L, const int64_t *tile, int32_t n_tile,
+                       tla_layout *out);
+
+/*
+ * tiled_divide: logical_divide, then the inside-tile leaves gathered into
+ * mode 0 and each tile-index leaf a mode of its own:
+ * ((tile_0, tile_1, ...), rest_0, rest_1, ...).  Host only.
+ */
+int tla_tiled_divide(const tla_layout *L, const int64_t *tile, int32_t n_tile,
+                     tla_layout *out);
+
+/*
+ * The strip-mined thread map of an R x C tile, T threads, V contiguous
+ * elements per access, I iterations per thread, as a TV layout
+ *   ((G, T/G), (V, I)) : ((V, Q), (1, S*Q))
+ * into the tile index, with Q the contiguous extent (C when
+ * contiguous_dim == 1: index row*C + col; R when contiguous_dim == 0:
+ * index row + col*R), G = Q/V column groups, S = (strided extent)/I the
+ * row stride.  Requires R*C == T*V*I, V | Q, G | T and S == T/G
+ * (TLA_ERR_INVALID_ARG otherwise).  Host only.
+ */
+int tla_thread_map(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I,
+                   int32_t contiguous_dim, tla_layout *out);
+
+/*
+ * Runs the device-side strip-mined thread map the copy kernels use, for
+ * every (t, it, v) with t < T, it < I, v < V, at index
+ * i = t + T*(v + V*it):
+ *   out_index[i] = tile index of the element (as tla_thread_map),
+ *   out_valid[i] = 1 if the element lies inside the first rows_valid rows
+ *                  and cols_valid columns of the tile, else 0.
+ * out_index: device int64[T*V*I]; out_valid: device uint8[T*V*I] or NULL.
+ * Same argument rules as tla_thread_map; rows_valid, cols_valid >= 0.
+ */
+int tla_thread_map_eval(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I,
+                        int32_t contiguous_dim, int64_t rows_valid, int64_t cols_valid,
+                        int64_t *out_index, uint8_t *out_valid, void *stream);
+
+/* ------------------------------------------------------------- misc */
+const char *tla_status_string(int status);
+int tla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TLA_H */

@@ -1,0 +1,204 @@
+"""The C ABI without a GPU: the library loads and exports every function
+include/tla.h declares; argument errors come back as status codes before
+any device work; the host-side descriptor builders (logical/tiled divide,
+thread map) agree with the oracle's definitions."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_layout_algebra_amd as tla
+from oracle import layout as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tla.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tla_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tla.lib()
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(tla.EXPORTED) == names
+    assert tla.version() == 1
+    for code, name in [(0, "TLA_OK"), (-1, "TLA_ERR_INVALID_ARG"), (-2, "TLA_ERR_UNSUPPORTED"),
+                       (-3, "TLA_ERR_OVERLAP"), (-4, "TLA_ERR_HIP")]:
+        assert tla.status_string(code) == name
+
+
+FAKE = 1 << 20  # an aligned address that is never dereferenced on these paths
+
+
+def _args(**kw):
+    base = dict(M=64, N=64, K=64, A=FAKE, a_type=tla.BF16, a_order=tla.ROW_MAJOR, lda=64,
+                B=FAKE, b_type=tla.BF16, b_order=tla.COL_MAJOR, ldb=64,
+                C=None, c_type=tla.BF16, c_order=tla.ROW_MAJOR, ldc=64,
+                D=FAKE, d_type=tla.BF16, d_order=tla.ROW_MAJOR, ldd=64,
+                bias=None, bias_type=tla.BF16, act=tla.ACT_NONE,
+                alpha=1.0, beta=0.0, scale_a=1.0, scale_b=1.0)
+    base.update(kw)
+    return tla.GemmArgs(**base)
+
+
+def _variant(a):
+    buf = ctypes.create_string_buffer(64)
+    rc = tla.lib().tla_gemm_variant(ctypes.byref(a), buf, 64)
+    return rc, buf.value.decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), tla.ERR_INVALID_ARG),
+    (dict(K=-5), tla.ERR_INVALID_ARG),
+    (dict(a_order=7), tla.ERR_INVALID_ARG),
+    (dict(act=9), tla.ERR_INVALID_ARG),
+    (dict(b_type=tla.F16), tla.ERR_UNSUPPORTED),
+    (dict(a_type=tla.F32, b_type=tla.F32), tla.ERR_UNSUPPORTED),
+    (dict(d_type=tla.E4M3), tla.ERR_UNSUPPORTED),
+    (dict(beta=0.5), tla.ERR_INVALID_ARG),                 # C missing
+    (dict(beta=0.5, C=FAKE, c_type=tla.E4M3), tla.ERR_UNSUPPORTED),
+    (dict(bias=FAKE, bias_type=tla.E4M3), tla.ERR_UNSUPPORTED),
+    (dict(D=None), tla.ERR_INVALID_ARG),
+    (dict(A=None), tla.ERR_INVALID_ARG),
+    (dict(lda=63), tla.ERR_INVALID_ARG),                   # row-major A needs lda >= K
+    (dict(a_order=tla.COL_MAJOR, lda=63), tla.ERR_INVALID_ARG),
+    (dict(ldb=10), tla.ERR_INVALID_ARG),
+    (dict(ldd=3), tla.ERR_INVALID_ARG),
+    (dict(beta=1.0, C=FAKE, ldc=8), tla.ERR_INVALID_ARG),
+    (dict(beta=1.0, C=FAKE, c_order=tla.COL_MAJOR), tla.ERR_INVALID_ARG),  # aliases D, other order
+])
+def test_gemm_argument_errors(kw, status):
+    a = _args(**kw)
+    assert tla.gemm_epilogue_args(a, None) == status
+    assert _variant(a)[0] == status
+
+
+def test_gemm_null_args_and_noops():
+    assert tla.lib().tla_gemm_epilogue(None, None) == tla.ERR_INVALID_ARG
+    # M == 0 / N == 0 are no-ops even with NULL pointers
+    assert tla.gemm_epilogue_args(_args(M=0, A=None, B=None, D=None), None) == tla.OK
+    assert tla.gemm_epilogue_args(_args(N=0, A=None, B=None, D=None), None) == tla.OK
+    assert _variant(_args(M=0))[1] == "noop"
+    # K == 0 needs no A/B and no lda/ldb
+    assert _variant(_args(K=0, A=None, B=None, lda=0, ldb=0)) == (0, "gemm_general_128x128")
+
+
+def test_gemm_variant_choice():
+    # aligned K-contiguous operands with K a multiple of the slab width: fast
+    assert _variant(_args(M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldd=4096))[1] == "gemm_fast_256x256"
+    assert _variant(_args(M=256, N=256, K=256, lda=256, ldb=256, ldd=256))[1] == "gemm_fast_128x128"
+    e4 = dict(a_type=tla.E4M3, b_type=tla.E4M3, M=8192, N=8192, K=8192, lda=8192, ldb=8192, ldd=8192)
+    assert _variant(_args(**e4))[1] == "gemm_fast_256x256"
+    # fp8 slabs are 128 elements wide: K = 64 is ragged for e4m3
+    assert _variant(_args(**dict(e4, K=64, lda=64, ldb=64)))[1] == "gemm_general_128x128"
+    # N-contiguous B, odd pitches, misaligned bases, ragged K: general
+    assert _variant(_args(b_order=tla.ROW_MAJOR))[1] == "gemm_general_128x128"
+    assert _variant(_args(lda=65))[1] == "gemm_general_128x128"
+    assert _variant(_args(A=FAKE + 2))[1] == "gemm_general_128x128"
+    assert _variant(_args(K=63, lda=64, ldb=64))[1] == "gemm_general_128x128"
+
+
+def test_transpose_argument_errors():
+    f = tla.lib().tla_tiled_transpose
+    assert f(FAKE, 8, FAKE * 4, 8, -1, 8, 4, None) == tla.ERR_INVALID_ARG
+    assert f(FAKE, 8, FAKE * 4, 8, 8, 8, 3, None) == tla.ERR_UNSUPPORTED
+    assert f(FAKE, 8, FAKE * 4, 8, 0, 8, 4, None) == tla.OK          # empty
+    assert f(None, 8, FAKE * 4, 8, 8, 8, 4, None) == tla.ERR_INVALID_ARG
+    assert f(FAKE, 7, FAKE * 4, 8, 8, 8, 4, None) == tla.ERR_INVALID_ARG  # ld_src < N
+    assert f(FAKE, 8, FAKE * 4, 7, 8, 8, 4, None) == tla.ERR_INVALID_ARG  # ld_dst < M
+    assert f(FAKE + 2, 8, FAKE * 4, 8, 8, 8, 4, None) == tla.ERR_INVALID_ARG  # misaligned
+    assert f(FAKE, 8, FAKE + 64, 8, 8, 8, 4, None) == tla.ERR_OVERLAP
+    assert f(FAKE + 64, 8, FAKE, 8, 8, 8, 4, None) == tla.ERR_OVERLAP
+
+
+def _eval_desc(d):
+    shape, stride = tla.layout_tuple(d)
+    return L.Layout(shape, stride)
+
+
+def test_layout_size_and_descriptor_round_trip():
+    d = tla.make_layout(((4, 8), (2, 2, 2)), ((32, 1), (16, 8, 128)))
+    assert tla.layout_size(d) == 256
+    assert tla.layout_tuple(d) == (((4, 8), (2, 2, 2)), ((32, 1), (16, 8, 128)))
+    bad = tla.make_layout((4, 0), (1, 4))
+    with pytest.raises(tla.TlaError):
+        tla.layout_size(bad)
+
+
+@pytest.mark.parametrize("shape,stride,tile", [
+    ((1024,), (1,), (128,)),
+    ((10, 7), (7, 1), (4, 3)),
+    ((96, 64), (64, 1), (32, 32)),
+    ((5, 6, 7), (1, 5, 30), (2, 3, 4)),
+    ((16384, 16384), (16384, 1), (32, 32)),
+])
+def test_divide_descriptors_match_oracle(shape, stride, tile):
+    d = tla.make_layout(shape, stride)
+    ld = tla.logical_divide(d, tile)
+    td = tla.tiled_divide(d, tile)
+    o_ld = L.logical_divide(L.Layout(shape, stride), tile)
+    o_td = L.tiled_divide(L.Layout(shape, stride), tile)
+    ev_ld, ev_td = _eval_desc(ld), _eval_desc(td)
+    # same leaves in the same order (a one-leaf mode prints as an int)
+    assert L.flatten(ev_ld.shape) == L.flatten(o_ld.shape)
+    assert L.flatten(ev_td.shape) == L.flatten(o_td.shape)
+    n = o_ld.size()
+    idxs = range(n) if n <= 5000 else range(0, n, n // 4999)
+    for i in idxs:
+        assert ev_ld(i) == o_ld(L.idx2crd(i, o_ld.shape))
+        assert ev_td(i) == o_td(L.idx2crd(i, o_td.shape))
+
+
+def test_divide_errors():
+    d = tla.make_layout(((2, 2), 4), ((1, 2), 4))  # nested: not flat
+    with pytest.raises(tla.TlaError):
+        tla.logical_divide(d, (2, 2))
+    with pytest.raises(tla.TlaError):
+        tla.logical_divide(tla.make_layout((8,), (1,)), (0,))
+    with pytest.raises(tla.TlaError):
+        tla.logical_divide(tla.make_layout((8, 8), (8, 1)), (2,))
+
+
+@pytest.mark.parametrize("R,C,T,V,I,contig", [
+    (64, 64, 128, 4, 8, 1), (64, 64, 128, 4, 8, 0), (256, 8, 256, 1, 8, 1),
+    (128, 8, 256, 1, 4, 0), (32, 32, 256, 1, 4, 1), (16, 16, 64, 4, 1, 1),
+])
+def test_thread_map_descriptor_matches_oracle(R, C, T, V, I, contig):
+    d = tla.thread_map(R, C, T, V, I, contig)
+    tm = L.StripMinedThreadMap(R, C, T, V, I, contig)
+    ev = _eval_desc(d)
+    assert ev.shape == tm.tv_layout().shape and ev.stride == tm.tv_layout().stride
+    assert ev.table() == tm.table()
+
+
+@pytest.mark.parametrize("args", [
+    (64, 64, 128, 4, 4, 1),   # tile equation violated
+    (64, 60, 120, 8, 4, 1),   # V does not divide C
+    (64, 64, 128, 4, 8, 2),   # bad contiguous dim
+    (0, 64, 128, 4, 8, 1),
+])
+def test_thread_map_errors(args):
+    with pytest.raises(tla.TlaError):
+        tla.thread_map(*args)
+    assert tla.lib().tla_thread_map_eval(*args, 64, 64, FAKE, None, None) == tla.ERR_INVALID_ARG
+
+
+def test_layout_eval_argument_errors():
+    f = tla.lib().tla_layout_eval
+    outer = tla.make_layout((4, 8), (8, 1))
+    inner = tla.make_layout((8, 4), (4, 1))
+    assert f(ctypes.byref(outer), None, FAKE, 31, None) == tla.ERR_INVALID_ARG   # n != size
+    assert f(ctypes.byref(outer), None, None, 32, None) == tla.ERR_INVALID_ARG   # out NULL
+    big = tla.make_layout((8, 8), (8, 1))                                        # reaches 63 >= 32
+    assert f(ctypes.byref(outer), ctypes.byref(big), FAKE, 64, None) == tla.ERR_INVALID_ARG
+    neg = tla.make_layout((4,), (-1,))
+    assert f(ctypes.byref(outer), ctypes.byref(neg), FAKE, 4, None) == tla.ERR_INVALID_ARG
+    assert f(ctypes.byref(outer), ctypes.byref(inner), FAKE, 31, None) == tla.ERR_INVALID_ARG
+    assert f(None, None, FAKE, 1, None) == tla.ERR_INVALID_ARG

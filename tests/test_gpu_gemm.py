@@ -1,0 +1,238 @@
+"""GEMM + epilogue parity: the HIP path through the C ABI against the
+oracle on the same seeded inputs.
+
+* integer-valued inputs: every partial sum is exact in fp32, so D must equal
+  the oracle's exact result rounded to D's type, bit for bit;
+* the measured workloads at reduced sizes (full comparison) and at full size
+  (sampled outputs, including every tile-boundary row and column);
+* edge cases: K = 0, ragged edges on every side, pitched operands with NaN
+  padding, sentinel-filled output padding, misaligned bases, C aliasing D,
+  column-major C and D, fp32 C and bias.
+Tolerance: |D - ref| <= tol*(1 + |ref|), tol 1e-2 (fp16/bf16), 5e-2 (fp8).
+"""
+import dataclasses
+import itertools
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import gemm as og
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+SENT = {W.F16: 0x5A5A, W.BF16: 0x5A5A}
+
+
+def _logical(case, D):
+    return og.decode(case.d_type, W.d_logical(case, D).copy())
+
+
+def _check_full(case, inp, **kw):
+    D = G.run_gemm(case, inp, sentinel=SENT[case.d_type], **kw)
+    assert G.padding_untouched(case, D, SENT[case.d_type])
+    got = _logical(case, D)
+    ref = G.oracle_ref(case, inp)
+    ok, worst = og.within_tolerance(got, ref, case.tol)
+    assert ok, "%s: worst |D-ref|/(1+|ref|) = %g > %g" % (case.name, worst, case.tol)
+    return worst
+
+
+def _sample(case, rng, tile=256):
+    rows = {0, 1, case.M - 1}
+    cols = {0, 1, case.N - 1}
+    for t in range(tile, case.M, tile):
+        rows |= {t - 1, t}
+    for t in range(tile, case.N, tile):
+        cols |= {t - 1, t}
+    rows |= set(rng.integers(0, case.M, 16).tolist())
+    cols |= set(rng.integers(0, case.N, 8).tolist())
+    rows, cols = sorted(r for r in rows if r < case.M), sorted(c for c in cols if c < case.N)
+    ms = [m for m in rows for _ in range(case.N)]
+    ns = [n for _ in rows for n in range(case.N)]
+    ms += [m for _ in cols for m in range(case.M)]
+    ns += [n for n in cols for _ in range(case.M)]
+    ms += rng.integers(0, case.M, 4096).tolist()
+    ns += rng.integers(0, case.N, 4096).tolist()
+    return np.array(ms, dtype=np.int64), np.array(ns, dtype=np.int64)
+
+
+def _check_sampled(case, inp, seed=0):
+    D = G.run_gemm(case, inp, sentinel=SENT[case.d_type])
+    assert G.padding_untouched(case, D, SENT[case.d_type])
+    got = _logical(case, D)
+    ms, ns = _sample(case, np.random.default_rng(seed))
+    ref = G.oracle_points(case, inp, ms, ns)
+    ok, worst = og.within_tolerance(got[ms, ns], ref, case.tol)
+    assert ok, "%s: worst |D-ref|/(1+|ref|) = %g > %g" % (case.name, worst, case.tol)
+    assert not np.isnan(got).any()
+    return worst
+
+
+# ------------------------------------------------------------ bit-exact set
+
+EXACT_SIZES = [(1, 1, 1), (2, 3, 5), (13, 17, 31), (33, 65, 64), (65, 33, 17), (64, 64, 64),
+               (128, 128, 128), (131, 67, 200), (256, 256, 256)]
+ORDERS = list(itertools.product([W.ROW, W.COL], repeat=2))
+
+
+@pytest.mark.parametrize("a_type,d_type", [(W.F16, W.F16), (W.BF16, W.BF16), (W.E4M3, W.BF16)])
+@pytest.mark.parametrize("M,N,K", EXACT_SIZES)
+def test_integer_inputs_bit_exact(M, N, K, a_type, d_type):
+    for (a_order, b_order), act in zip(ORDERS, [W.ACT_NONE, W.ACT_RELU, W.ACT_NONE, W.ACT_RELU]):
+        case = W.GemmCase(name="exact", M=M, N=N, K=K, a_type=a_type, b_type=a_type,
+                          d_type=d_type, a_order=a_order, b_order=b_order, alpha=1.5, beta=0.5,
+                          act=act, has_c=True, has_bias=True, seed=M * 1000 + N + K,
+                          dist_a="int3", dist_b="int3", dist_c="int3", dist_bias="eighths")
+        inp = W.gemm_inputs(case)
+        D = G.run_gemm(case, inp, sentinel=SENT[d_type])
+        ref = G.oracle_ref(case, inp)
+        want = W.encode(ref, d_type).reshape(M, N)
+        got = W.d_logical(case, D)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, "%s orders %s: %d mismatches, first at %s (variant %s)" % (
+            (M, N, K), (a_order, b_order), len(bad), bad[0], G.variant(case))
+
+
+def test_exact_set_covers_both_paths():
+    seen = set()
+    for (M, N, K) in EXACT_SIZES:
+        for a_type in (W.F16, W.E4M3):
+            case = W.GemmCase(name="v", M=M, N=N, K=K, a_type=a_type, b_type=a_type,
+                              d_type=W.BF16)
+            seen.add(G.variant(case))
+    assert {"gemm_fast_128x128", "gemm_general_128x128"} <= seen
+
+
+# --------------------------------------------------- measured workloads
+
+def test_f16_256_full():
+    case = W.GEMM_F16_256
+    assert G.variant(case) == "gemm_fast_128x128"
+    _check_full(case, W.gemm_inputs(case))
+
+
+def test_bf16_epilogue_reduced_full():
+    case = dataclasses.replace(W.GEMM_BF16_4096, M=512, N=768, K=1024, lda=0, ldb=0, ldc=0, ldd=0)
+    case.__post_init__()
+    _check_full(case, W.gemm_inputs(case))
+
+
+def test_bf16_fast256_ragged_edges():
+    # 8 x 16 tiles of 256 take the 256x256 fast path; M and N end mid-tile
+    case = dataclasses.replace(W.GEMM_BF16_4096, M=2000, N=4000, K=256, lda=0, ldb=0, ldc=0, ldd=0)
+    case.__post_init__()
+    assert G.variant(case) == "gemm_fast_256x256"
+    _check_full(case, W.gemm_inputs(case))
+
+
+def test_bf16_4096_full_size_sampled():
+    case = W.GEMM_BF16_4096
+    assert G.variant(case) == "gemm_fast_256x256"
+    _check_sampled(case, W.gemm_inputs(case))
+
+
+def test_f16_ragged_reduced_full():
+    case = dataclasses.replace(W.GEMM_F16_RAGGED, M=301, N=409, K=77, lda=0, ldb=0, ldc=0, ldd=0)
+    case.__post_init__()
+    _check_full(case, W.gemm_inputs(case))
+
+
+def test_f16_ragged_full_size():
+    case = W.GEMM_F16_RAGGED
+    assert G.variant(case) == "gemm_general_128x128"
+    _check_full(case, W.gemm_inputs(case))
+
+
+def test_e4m3_gelu_reduced_full():
+    case = dataclasses.replace(W.GEMM_E4M3_8192, M=1024, N=768, K=1024, lda=0, ldb=0, ldc=0, ldd=0)
+    case.__post_init__()
+    assert G.variant(case) == "gemm_fast_128x128"
+    _check_full(case, W.gemm_inputs(case))
+
+
+def test_e4m3_general_path_ragged_k():
+    case = dataclasses.replace(W.GEMM_E4M3_8192, M=300, N=200, K=200, lda=0, ldb=0, ldc=0, ldd=0)
+    case.__post_init__()
+    assert G.variant(case) == "gemm_general_128x128"
+    _check_full(case, W.gemm_inputs(case))
+
+
+def test_e4m3_8192_full_size_sampled():
+    case = W.GEMM_E4M3_8192
+    assert G.variant(case) == "gemm_fast_256x256"
+    _check_sampled(case, W.gemm_inputs(case))
+
+
+# ------------------------------------------------------------- edge cases
+
+def _small(**kw):
+    base = dict(name="edge", M=70, N=90, K=100, a_type=W.BF16, b_type=W.BF16, d_type=W.BF16,
+                alpha=1.25, beta=0.75, has_c=True, has_bias=True, act=W.ACT_GELU, seed=5)
+    base.update(kw)
+    return W.GemmCase(**base)
+
+
+@pytest.mark.parametrize("a_order,b_order", ORDERS)
+@pytest.mark.parametrize("a_type", [W.F16, W.BF16, W.E4M3])
+def test_pitched_operands_nan_padding(a_order, b_order, a_type):
+    case = _small(a_order=a_order, b_order=b_order, a_type=a_type, b_type=a_type,
+                  d_type=W.F16 if a_type == W.F16 else W.BF16)
+    case.lda += 8
+    case.ldb += 3
+    case.ldc += 5
+    case.ldd += 7
+    _check_full(case, W.gemm_inputs(case))  # NaN padding would poison D
+
+
+def test_fast_path_pitched():
+    case = _small(M=256, N=384, K=256, act=W.ACT_RELU)
+    case.lda, case.ldb, case.ldc, case.ldd = 256 + 64, 256 + 8, 384 + 4, 384 + 12
+    assert G.variant(case) == "gemm_fast_128x128"
+    _check_full(case, W.gemm_inputs(case))
+
+
+def test_k_zero():
+    case = _small(K=0, act=W.ACT_RELU)
+    case.lda = case.ldb = 1
+    inp = W.gemm_inputs(case)
+    inp["A"] = inp["B"] = None
+    _check_full(case, inp)
+
+
+def test_misaligned_bases_take_general_path():
+    case = _small(M=128, N=128, K=128)
+    _check_full(case, W.gemm_inputs(case), pad_front=1)
+
+
+def test_c_aliases_d():
+    case = _small(M=200, N=136, K=64)
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, d_is_c=True)
+    got = _logical(case, D)
+    ok, worst = og.within_tolerance(got, G.oracle_ref(case, inp), case.tol)
+    assert ok, worst
+
+
+@pytest.mark.parametrize("c_order,d_order", [(W.COL, W.ROW), (W.ROW, W.COL), (W.COL, W.COL)])
+def test_column_major_c_and_d(c_order, d_order):
+    case = _small(c_order=c_order, d_order=d_order)
+    case.ldc = case.M if c_order == W.COL else case.N
+    case.ldd = (case.M if d_order == W.COL else case.N) + 2
+    _check_full(case, W.gemm_inputs(case))
+
+
+def test_fp32_c_and_bias():
+    case = _small(M=256, N=256, K=128, c_type=W.F32, bias_type=W.F32, act=W.ACT_NONE)
+    _check_full(case, W.gemm_inputs(case))
+
+
+def test_beta_zero_without_c():
+    case = _small(beta=0.0, has_c=False)
+    _check_full(case, W.gemm_inputs(case))
+
+
+def test_repeatable():
+    case = _small(M=512, N=512, K=512, act=W.ACT_NONE)
+    inp = W.gemm_inputs(case)
+    assert np.array_equal(G.run_gemm(case, inp), G.run_gemm(case, inp))

@@ -1,0 +1,462 @@
+// gemm.hip -- hierarchically tiled GEMM with a fused epilogue for gfx950.
+//
+//   D = act(alpha_eff * A.B + beta*C + bias),  fp32 accumulation.
+//
+// Three levels of tiling, as in "CUTLASS / CuTe 主线" (hpc.payai.win/cutlass),
+// section 一: a workgroup owns a BM x BN tile of D (the block tile), each of
+// its four 64-lane wavefronts a (BM/2) x (BN/2) quarter (the wave tile), and
+// each 32x32 MFMA instruction a 32x32 piece of that (the instruction tile).
+// The K loop (section 二's mainloop: global -> shared -> register) moves one
+// 128-byte-wide K slab of A and of B per step into LDS (64 bf16/fp16 or 128
+// e4m3 per row), double-buffered so the next slab streams in while the
+// current one feeds the matrix cores (section 四: pipeline stages hide global
+// latency).  The epilogue applies alpha, beta*C, bias and the activation to
+// the fp32 accumulators in registers and stores D once (section 四: fuse
+// before the store).
+//
+// Operand roles.  Both LDS slabs hold rows of K (A by m, B by n).  The MFMA
+// is issued with the B rows as its first operand and the A rows as its
+// second, so its 32x32 result is D^T: each lane then owns four consecutive
+// columns of one row of D, which the epilogue reads (C) and writes (D) as
+// 8-byte vectors.
+//
+// Two load paths feed the same LDS layout:
+//   fast    both operands K-contiguous, 16-byte aligned rows, K a multiple of
+//           the slab width: each lane issues global_load_lds_dwordx4, a
+//           direct HBM -> LDS copy that lands lane-linearly; the LDS XOR
+//           swizzle is applied by permuting which global chunk each lane
+//           fetches.  Rows past M or N are clamped to the last real row (their
+//           results are never stored), so the loop carries no predicates.
+//   general any order, pitch or alignment, ragged K: registers staged through
+//           a strip-mined thread map with per-element predicates; elements
+//           outside the matrix load as zero.
+#include "kernels.hpp"
+#include "tla/copy.hpp"
+#include "tla/layout.hpp"
+#include "tla/mfma.hpp"
+
+namespace tla {
+namespace {
+
+constexpr int kThreads = 256;  // four wavefronts
+constexpr int kRowBytes = 128; // K bytes per LDS row per k-tile
+constexpr int kChunks = kRowBytes / 16;
+// f(row) = (row >> 1) & 7: the 16 rows a quarter-wave reads at one logical
+// chunk cover all 16 distinct 16-byte bank groups of a 256-byte LDS window.
+using Swz = XorSwizzle<kChunks, 1>;
+
+enum : int { kCVec = 1, kDVec = 2, kBiasVec = 4 };
+
+struct GemmParams {
+  const uint8_t* A;
+  const uint8_t* B;
+  const uint8_t* C;
+  uint8_t* D;
+  const uint8_t* bias;
+  // (row, k) strides of the A view (rows = m) and the B view (rows = n), in
+  // elements; (m, n) strides of C and D.
+  int64_t a_sr, a_sk, b_sr, b_sk, c_sm, c_sn, d_sm, d_sn;
+  int M, N, K;
+  int c_type, d_type, bias_type, act;
+  float alpha, beta;
+  int tiles_m, tiles_n;
+  int flags;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ lds_void_t* to_lds(void* p) { return (lds_void_t*)(p); }
+
+// ---------------------------------------------------------- tile scheduler
+// Workgroup b is dispatched to XCD b % 8.  Tile ids are handed out so that
+// each XCD gets a contiguous run of them, and runs are ordered GROUP_M tile
+// rows at a time (tile row fastest), so the workgroups sharing one XCD's L2
+// work on a compact block of D and reuse each other's A and B slabs.
+__device__ __forceinline__ void schedule(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int kXcds = 8, kGroupM = 4;
+  const int total = tiles_m * tiles_n;
+  int id = bid;
+  if (total % kXcds == 0) id = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+  const int per_group = kGroupM * tiles_n;
+  const int first_m = (id / per_group) * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in = id % per_group;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+// ------------------------------------------------------------ fast loader
+// One k-tile slab of ROWS rows x 128 bytes via direct global -> LDS copies.
+// The strip-mined map (ROWS x 8 chunks, 256 threads, one chunk per access)
+// puts thread t of iteration it at LDS slot t + 256*it, which is exactly the
+// lane-linear slot the DMA writes; the lane fetches the logical chunk that
+// the swizzle assigns to that slot.
+template <int ROWS>
+__device__ __forceinline__ void dma_slab(const uint8_t* __restrict__ base, int64_t row_bytes,
+                                         int row0, int rows_valid, int64_t kbyte0, uint8_t* slab,
+                                         int tid) {
+  constexpr StripMinedMap map(ROWS, kChunks, kThreads, 1, ROWS * kChunks / kThreads);
+  static_assert(map.well_formed(), "slab thread map");
+#pragma unroll
+  for (int it = 0; it < map.I; ++it) {
+    const int r = map.strided(tid, it);
+    const int c = Swz::chunk(r, map.contiguous(tid, 0));
+    const int gr = min(row0 + r, rows_valid - 1);
+    const uint8_t* src = base + gr * row_bytes + kbyte0 + c * 16;
+    uint8_t* dst = slab + map.index(tid & ~63, it, 0) * 16;  // wave-uniform
+    __builtin_amdgcn_global_load_lds(src, to_lds(dst), 16, 0, 0);
+  }
+}
+
+// --------------------------------------------------------- general loader
+// Element-predicated, register-staged slab copy for any operand view
+// (row, k) -> row*s_r + k*s_k.  K-contiguous views use the row-contiguous
+// thread map (consecutive lanes walk K); the others use the column-major
+// variant (consecutive lanes walk rows, so each element load coalesces).
+template <int ROWS, int EB>
+struct RegSlab {
+  static constexpr int kI = ROWS * kChunks / kThreads;
+  static constexpr int kCE = 16 / EB;  // elements per 16-byte chunk
+  i32x4 v[kI];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t s_r, int64_t s_k,
+                                       int row0, int rows_valid, int k0, int K, bool vec_ok,
+                                       int tid) {
+    constexpr StripMinedMap kmap(ROWS, kChunks, kThreads, 1, kI, 1);
+    constexpr StripMinedMap rmap(ROWS, kChunks, kThreads, 1, kI, 0);
+    static_assert(kmap.well_formed() && rmap.well_formed(), "slab thread maps");
+    const bool kcontig = (s_k == 1);
+#pragma unroll
+    for (int it = 0; it < kI; ++it) {
+      const int r = kcontig ? kmap.row(tid, it, 0) : rmap.row(tid, it, 0);
+      const int c = kcontig ? kmap.col(tid, it, 0) : rmap.col(tid, it, 0);
+      const int gr = row0 + r;
+      const int gk = k0 + c * kCE;
+      i32x4 x = {0, 0, 0, 0};
+      if (gr < rows_valid) {
+        const uint8_t* p = base + (gr * s_r + (int64_t)gk * s_k) * EB;
+        if (vec_ok && kcontig && gk + kCE <= K) {
+          x = *(const i32x4*)p;
+        } else {
+          uint8_t bytes[16] = {};
+#pragma unroll
+          for (int e = 0; e < kCE; ++e) {
+            if (gk + e < K) {
+              const uint8_t* q = p + (int64_t)e * s_k * EB;
+#pragma unroll
+              for (int b = 0; b < EB; ++b) bytes[e * EB + b] = q[b];
+            }
+          }
+          x = __builtin_bit_cast(i32x4, bytes);
+        }
+      }
+      v[it] = x;
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* slab, bool kcontig, int tid) const {
+    constexpr StripMinedMap kmap(ROWS, kChunks, kThreads, 1, kI, 1);
+    constexpr StripMinedMap rmap(ROWS, kChunks, kThreads, 1, kI, 0);
+#pragma unroll
+    for (int it = 0; it < kI; ++it) {
+      const int r = kcontig ? kmap.row(tid, it, 0) : rmap.row(tid, it, 0);
+      const int c = kcontig ? kmap.col(tid, it, 0) : rmap.col(tid, it, 0);
+      *(i32x4*)(slab + r * kRowBytes + Swz::chunk(r, c) * 16) = v[it];
+    }
+  }
+};
+
+// ------------------------------------------------------- fragment loader
+// Lane l's operand fragment for MFMA k-step ks: row `row` of the slab, the
+// (l/32)-th kLaneBytes-wide half of the step's K bytes.
+template <int kCode>
+__device__ __forceinline__ typename MfmaAtom<kCode>::Frag load_frag(const uint8_t* slab, int row,
+                                                                   int ks, int lane) {
+  using Atom = MfmaAtom<kCode>;
+  constexpr int kStepBytes = Atom::kK * elem_bytes(kCode);
+  const int c0 = (ks * kStepBytes + (lane >> 5) * Atom::kLaneBytes) / 16;
+  const uint8_t* rowp = slab + row * kRowBytes;
+  if constexpr (Atom::kLaneBytes == 16) {
+    return *(const i32x4*)(rowp + Swz::chunk(row, c0) * 16);
+  } else {
+    i32x4 lo = *(const i32x4*)(rowp + Swz::chunk(row, c0) * 16);
+    i32x4 hi = *(const i32x4*)(rowp + Swz::chunk(row, c0 + 1) * 16);
+    return typename Atom::Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+// ---------------------------------------------------------------- epilogue
+__device__ __forceinline__ float load_elem(const uint8_t* p, int type, int64_t idx) {
+  if (type == kF32) return ((const float*)p)[idx];
+  const uint16_t h = ((const uint16_t*)p)[idx];
+  if (type == kBF16) return __builtin_bit_cast(float, (uint32_t)h << 16);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ uint16_t to_bits(float v, int type) {
+  if (type == kBF16) return __builtin_bit_cast(uint16_t, (__bf16)v);
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+__device__ __forceinline__ void load4(const uint8_t* p, int type, int64_t idx, float (&x)[4]) {
+  if (type == kF32) {
+    const f32x4 v = *(const f32x4*)((const float*)p + idx);
+    x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+  } else {
+    const uint2 u = *(const uint2*)((const uint16_t*)p + idx);
+    const uint32_t w[4] = {u.x & 0xFFFFu, u.x >> 16, u.y & 0xFFFFu, u.y >> 16};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      x[q] = (type == kBF16) ? __builtin_bit_cast(float, w[q] << 16)
+                             : (float)__builtin_bit_cast(_Float16, (uint16_t)w[q]);
+  }
+}
+
+__device__ __forceinline__ float activate(float y, int act) {
+  if (act == TLA_ACT_RELU) return y > 0.f ? y : 0.f;
+  if (act == TLA_ACT_GELU) return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f));
+  return y;
+}
+
+// Four consecutive columns n..n+3 of row m.
+__device__ __forceinline__ void epilogue4(const GemmParams& p, int m, int n, const float (&acc)[4]) {
+  if (m >= p.M || n >= p.N) return;
+  const bool full = n + 3 < p.N;
+  float y[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) y[q] = p.alpha * acc[q];
+  if (p.beta != 0.f) {
+    float c[4] = {0.f, 0.f, 0.f, 0.f};
+    if (full && (p.flags & kCVec)) {
+      load4(p.C, p.c_type, m * p.c_sm + (int64_t)n, c);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (n + q < p.N) c[q] = load_elem(p.C, p.c_type, m * p.c_sm + (int64_t)(n + q) * p.c_sn);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] += p.beta * c[q];
+  }
+  if (p.bias) {
+    float b[4] = {0.f, 0.f, 0.f, 0.f};
+    if (full && (p.flags & kBiasVec)) {
+      load4(p.bias, p.bias_type, n, b);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (n + q < p.N) b[q] = load_elem(p.bias, p.bias_type, n + q);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] += b[q];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) y[q] = activate(y[q], p.act);
+  uint16_t* D = (uint16_t*)p.D;
+  if (full && (p.flags & kDVec)) {
+    uint2 u;
+    u.x = (uint32_t)to_bits(y[0], p.d_type) | ((uint32_t)to_bits(y[1], p.d_type) << 16);
+    u.y = (uint32_t)to_bits(y[2], p.d_type) | ((uint32_t)to_bits(y[3], p.d_type) << 16);
+    *(uint2*)(D + m * p.d_sm + n) = u;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (n + q < p.N) D[m * p.d_sm + (int64_t)(n + q) * p.d_sn] = to_bits(y[q], p.d_type);
+  }
+}
+
+// ------------------------------------------------------------------ kernel
+template <int kCode, int BM, int BN, bool kFast>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
+  using Atom = MfmaAtom<kCode>;
+  using Frag = typename Atom::Frag;
+  constexpr int EB = elem_bytes(kCode);
+  constexpr int BK = kRowBytes / EB;         // K elements per k-tile
+  constexpr int WM = BM / 2, WN = BN / 2;    // 2 x 2 wavefronts
+  constexpr int FM = WM / 32, FN = WN / 32;  // MFMA tiles per wave
+  constexpr int KSTEPS = BK / Atom::kK;
+  constexpr int SLAB_A = BM * kRowBytes, STAGE = (BM + BN) * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tm, tn;
+  schedule(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm0 = (wave & 1) * WM, wn0 = (wave >> 1) * WN;
+
+  f32x16 acc[FM][FN];
+  static_for<FM>([&](auto i) { static_for<FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
+
+  // One k-tile from LDS: the fragments of MFMA k-step ks+1 are read while
+  // the MFMAs of step ks run (two fragment buffers), so LDS latency hides
+  // behind matrix-core work.
+  auto compute = [&](const uint8_t* stage) {
+    const uint8_t* sa = stage;
+    const uint8_t* sb = stage + SLAB_A;
+    Frag a[2][FM], b[2][FN];
+    auto load = [&](auto buf, auto ks) {
+      static_for<FM>([&](auto i) { a[buf][i] = load_frag<kCode>(sa, wm0 + 32 * i + (lane & 31), ks, lane); });
+      static_for<FN>([&](auto j) { b[buf][j] = load_frag<kCode>(sb, wn0 + 32 * j + (lane & 31), ks, lane); });
+    };
+    load(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    static_for<KSTEPS>([&](auto ks) {
+      constexpr int cur = ks & 1;
+      if constexpr (ks + 1 < KSTEPS) load(std::integral_constant<int, cur ^ 1>{}, std::integral_constant<int, ks + 1>{});
+      static_for<FM>([&](auto i) { static_for<FN>([&](auto j) { Atom::mma(acc[i][j], b[cur][j], a[cur][i]); }); });
+    });
+    // Instruction order for the scheduler: the first step's fragment reads,
+    // then for each step its MFMAs interleaved with the next step's reads.
+    constexpr int kReads = (FM + FN) * (Atom::kLaneBytes / 16);
+    constexpr int kMfmas = FM * FN;
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+    static_for<KSTEPS - 1>([&](auto) {
+      static_for<kReads>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas / kReads > 0 ? kMfmas / kReads : 1, 0);
+      });
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmas, 0);
+  };
+
+  const int KT = (p.K + BK - 1) / BK;
+  if constexpr (kFast) {
+    const int64_t a_rb = p.a_sr * EB, b_rb = p.b_sr * EB;
+    if (KT > 0) {
+      dma_slab<BM>(p.A, a_rb, m0, p.M, 0, smem, tid);
+      dma_slab<BN>(p.B, b_rb, n0, p.N, 0, smem + SLAB_A, tid);
+    }
+    for (int kt = 0; kt < KT; ++kt) {
+      uint8_t* cur = smem + (kt & 1) * STAGE;
+      uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's copies of k-tile kt landed
+      __syncthreads();                     // ... and everyone's; stage nxt is no longer read
+      if (kt + 1 < KT) {
+        const int64_t kb = (int64_t)(kt + 1) * kRowBytes;
+        dma_slab<BM>(p.A, a_rb, m0, p.M, kb, nxt, tid);
+        dma_slab<BN>(p.B, b_rb, n0, p.N, kb, nxt + SLAB_A, tid);
+      }
+      compute(cur);
+    }
+  } else {
+    RegSlab<BM, EB> ra;
+    RegSlab<BN, EB> rb;
+    const bool a_vec = (p.flags >> 8) & 1, b_vec = (p.flags >> 9) & 1;
+    const bool a_kc = (p.a_sk == 1), b_kc = (p.b_sk == 1);
+    if (KT > 0) {
+      ra.load(p.A, p.a_sr, p.a_sk, m0, p.M, 0, p.K, a_vec, tid);
+      rb.load(p.B, p.b_sr, p.b_sk, n0, p.N, 0, p.K, b_vec, tid);
+      ra.store(smem, a_kc, tid);
+      rb.store(smem + SLAB_A, b_kc, tid);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      uint8_t* cur = smem + (kt & 1) * STAGE;
+      uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
+      if (kt + 1 < KT) {
+        ra.load(p.A, p.a_sr, p.a_sk, m0, p.M, (kt + 1) * BK, p.K, a_vec, tid);
+        rb.load(p.B, p.b_sr, p.b_sk, n0, p.N, (kt + 1) * BK, p.K, b_vec, tid);
+      }
+      compute(cur);
+      if (kt + 1 < KT) {
+        ra.store(nxt, a_kc, tid);
+        rb.store(nxt + SLAB_A, b_kc, tid);
+      }
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: acc[i][j] holds the D^T piece for rows m0+wm0+32i.. and
+  // columns n0+wn0+32j..; value r of lane l sits at (row, col) =
+  // (lane%32, mfma32_acc_row(l, r)) of that 32x32 piece.
+  static_for<FM>([&](auto i) {
+    const int m = m0 + wm0 + 32 * i + mfma32_acc_col(lane, 0);
+    static_for<FN>([&](auto j) {
+      static_for<4>([&](auto g) {
+        const int n = n0 + wn0 + 32 * j + mfma32_acc_row(lane, 4 * g);
+        const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                            acc[i][j][4 * g + 3]};
+        epilogue4(p, m, n, v);
+      });
+    });
+  });
+}
+
+// ----------------------------------------------------------------- dispatch
+template <int kCode, int BM, int BN, bool kFast>
+int launch(const GemmParams& p0, hipStream_t stream) {
+  GemmParams p = p0;
+  p.tiles_m = (p.M + BM - 1) / BM;
+  p.tiles_n = (p.N + BN - 1) / BN;
+  const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+  if (grid <= 0) return TLA_OK;
+  if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((gemm_kernel<kCode, BM, BN, kFast>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     stream, p);
+  return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
+}
+
+bool aligned(const void* p, int64_t bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
+
+template <int kCode>
+int dispatch_typed(const GemmProblem& g, const GemmParams& p, bool fast, bool big, hipStream_t s,
+                   bool dry, const char** name) {
+  static const char* names[4] = {"gemm_fast_256x256", "gemm_fast_128x128", "gemm_general_128x128",
+                                 "gemm_general_128x128"};
+  const int v = fast ? (big ? 0 : 1) : 2;
+  if (name) *name = names[v];
+  if (dry) return TLA_OK;
+  (void)g;
+  if (v == 0) return launch<kCode, 256, 256, true>(p, s);
+  if (v == 1) return launch<kCode, 128, 128, true>(p, s);
+  return launch<kCode, 128, 128, false>(p, s);
+}
+
+}  // namespace
+
+int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const char** name) {
+  if (g.M > 0x7FFFFFFF || g.N > 0x7FFFFFFF || g.K > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
+  const int eb = elem_bytes(g.a_type);
+  GemmParams p{};
+  p.A = (const uint8_t*)g.A;
+  p.B = (const uint8_t*)g.B;
+  p.C = (const uint8_t*)g.C;
+  p.D = (uint8_t*)g.D;
+  p.bias = (const uint8_t*)g.bias;
+  // operand views as (row, k) layouts: A rows are m, B rows are n
+  p.a_sr = g.a_order == TLA_ROW_MAJOR ? g.lda : 1;
+  p.a_sk = g.a_order == TLA_ROW_MAJOR ? 1 : g.lda;
+  p.b_sr = g.b_order == TLA_COL_MAJOR ? g.ldb : 1;
+  p.b_sk = g.b_order == TLA_COL_MAJOR ? 1 : g.ldb;
+  p.c_sm = g.c_order == TLA_ROW_MAJOR ? g.ldc : 1;
+  p.c_sn = g.c_order == TLA_ROW_MAJOR ? 1 : g.ldc;
+  p.d_sm = g.d_order == TLA_ROW_MAJOR ? g.ldd : 1;
+  p.d_sn = g.d_order == TLA_ROW_MAJOR ? 1 : g.ldd;
+  p.M = (int)g.M;
+  p.N = (int)g.N;
+  p.K = (int)g.K;
+  p.c_type = g.c_type;
+  p.d_type = g.d_type;
+  p.bias_type = g.bias_type;
+  p.act = g.act;
+  p.alpha = g.alpha_eff;
+  p.beta = g.beta;
+  if (!g.C) p.beta = 0.f;
+  const int ceb = elem_bytes(g.c_type), beb = elem_bytes(g.bias_type);
+  if (g.C && g.c_order == TLA_ROW_MAJOR && (g.ldc % 4) == 0 && aligned(g.C, 4 * ceb)) p.flags |= kCVec;
+  if (g.d_order == TLA_ROW_MAJOR && (g.ldd % 4) == 0 && aligned(g.D, 8)) p.flags |= kDVec;
+  if (g.bias && aligned(g.bias, 4 * beb)) p.flags |= kBiasVec;
+  const bool a_vec = (g.a_order == TLA_ROW_MAJOR) && ((g.lda * eb) % 16 == 0) && aligned(g.A, 16);
+  const bool b_vec = (g.b_order == TLA_COL_MAJOR) && ((g.ldb * eb) % 16 == 0) && aligned(g.B, 16);
+  p.flags |= (a_vec ? 1 << 8 : 0) | (b_vec ? 1 << 9 : 0);
+  const int BK = kRowBytes / eb;
+  const bool fast = a_vec && b_vec && g.K > 0 && (g.K % BK) == 0;
+  const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+  const bool big = tiles256 >= 128;
+  switch (g.a_type) {
+    case TLA_BF16: return dispatch_typed<kBF16>(g, p, fast, big, stream, dry_run, name);
+    case TLA_F16: return dispatch_typed<kF16>(g, p, fast, big, stream, dry_run, name);
+    case TLA_E4M3: return dispatch_typed<kE4M3>(g, p, fast, big, stream, dry_run, name);
+    default: return TLA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace tla

@@ -1,0 +1,46 @@
+// kernels.hpp -- internal launch interface between the C ABI (api.cpp) and
+// the HIP kernel files.  Every function here assumes its arguments were
+// validated by the ABI layer and returns a TLA_* status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tla.h"
+
+namespace tla {
+
+// A validated GEMM problem, in the element units of each operand.
+struct GemmProblem {
+  int64_t M, N, K;
+  const void* A; int a_type; int a_order; int64_t lda;
+  const void* B; int b_type; int b_order; int64_t ldb;
+  const void* C; int c_type; int c_order; int64_t ldc;
+  void* D; int d_type; int d_order; int64_t ldd;
+  const void* bias; int bias_type;
+  int act;
+  float alpha_eff;  // alpha * scale_a * scale_b
+  float beta;
+};
+
+// Picks the kernel variant; launches it unless `dry_run`.  `name` receives
+// the variant's name (may be NULL).
+int gemm_dispatch(const GemmProblem& p, hipStream_t stream, bool dry_run, const char** name);
+
+int transpose_dispatch(const void* src, int64_t ld_src, void* dst, int64_t ld_dst, int64_t M,
+                       int64_t N, int elem_bytes, hipStream_t stream);
+
+// Flat leaf lists of (validated) layouts; inner_leaves == 0 means no inner.
+struct FlatLayout {
+  int n;
+  int64_t shape[TLA_MAX_LEAVES];
+  int64_t stride[TLA_MAX_LEAVES];
+};
+int layout_eval_dispatch(const FlatLayout& outer, const FlatLayout& inner, bool has_inner,
+                         int64_t* out, int64_t n, hipStream_t stream);
+
+int thread_map_eval_dispatch(int R, int C, int T, int V, int I, int contig, int64_t rows_valid,
+                             int64_t cols_valid, int64_t* out_index, uint8_t* out_valid,
+                             hipStream_t stream);
+
+}  // namespace tla
