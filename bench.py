@@ -38,7 +38,41 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="append a plain 1 GiB device-to-device copy to every step (a kernel "
+                         "of known traffic, for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+CSRC = os.path.join(ROOT, "tiled_layout_algebra_amd", "csrc")
+_HEADERS = ["tla/layout.hpp", "tla/copy.hpp", "tla/mfma.hpp", "kernels.hpp"]
+
+
+def source_sha(kernel_file):
+    """First 16 hex digits of sha256 over a kernel source and the shared headers."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in [kernel_file] + _HEADERS:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def hbm_traffic(prefix, kernel_file):
+    """HBM bytes per launch recorded in profiles/hbm_traffic.txt for the kernel
+    whose label starts with `prefix`, if its sources are unchanged since the
+    counters were taken; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    sha = source_sha(kernel_file)
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 5 and not line.startswith("#") and parts[0].startswith(prefix) \
+                    and parts[1] == sha:
+                return int(parts[4])
+    return None
 
 
 def cpu_baseline(case, inp, target_s):
@@ -110,8 +144,18 @@ def main():
         tla.thread_map_eval(tmc.R, tmc.C, tmc.T, tmc.V, tmc.I, tmc.contiguous_dim, tmc.R - 1,
                             tmc.C, midx, mval, stream=stream.cuda_stream)
 
-    for _ in range(args.warmup):
+    if args.calibrate_copy:
+        csrc = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+        cdst = torch.empty_like(csrc)
+        csrc.fill_(1)
+
+    def step():
         gemm(); transpose(); tmap()
+        if args.calibrate_copy:
+            cdst.copy_(csrc)
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -126,6 +170,8 @@ def main():
         ev[s][2].record(stream)
         tmap()
         ev[s][3].record(stream)
+        if args.calibrate_copy:
+            cdst.copy_(csrc)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -155,12 +201,14 @@ def main():
                    "transpose": {"M": tc.M, "N": tc.N, "elem_bytes": 4, "seed": tc.seed}},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel_us": round(t_gemm.mean() * 1e6, 2),
+                     "traffic": hbm_traffic("gemm", "gemm.hip"),
+                     "kernel_us": round(t_gemm.mean() * 1e6, 2),
                      "kernel_us_min": round(t_gemm.min() * 1e6, 2)},
         "transpose": {"value": round(tr_gbs, 1), "unit": "GB/s",
                       "roofline": {"bound": "hbm", "achieved": round(tr_gbs, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                   "frac": round(tr_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                   "frac": round(tr_gbs / PEAK_HBM_GBS, 4),
+                                   "traffic": hbm_traffic("transpose", "transpose.hip"),
                                    "kernel_us": round(t_tr.mean() * 1e6, 2),
                                    "kernel_us_min": round(t_tr.min() * 1e6, 2)}},
     }

@@ -39,11 +39,38 @@ namespace tla {
 namespace {
 
 constexpr int kThreads = 256;  // four wavefronts
-constexpr int kRowBytes = 128; // K bytes per LDS row per k-tile
-constexpr int kChunks = kRowBytes / 16;
-// f(row) = (row >> 1) & 7: the 16 rows a quarter-wave reads at one logical
-// chunk cover all 16 distinct 16-byte bank groups of a 256-byte LDS window.
-using Swz = XorSwizzle<kChunks, 1>;
+
+// LDS slab geometry for rows of kRowBytes bytes of K (a power of two between
+// 32 and 128): kChunks 16-byte chunks per row and the XOR swizzle
+// f(row) = (row / rows-per-256-bytes) mod kChunks, so the 16 rows a
+// quarter-wave reads at one logical chunk cover the 16 distinct 16-byte
+// bank groups of a 256-byte LDS window.
+template <int kRowBytes>
+struct Slab {
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kRowShift = kRowBytes == 128 ? 1 : (kRowBytes == 64 ? 2 : 3);
+  using Swz = XorSwizzle<kChunks, kRowShift>;
+};
+
+// Workgroup barrier for LDS stages filled by direct copies.  __syncthreads()
+// would put a workgroup release fence in front of the barrier, and that fence
+// waits for every copy still in flight into LDS (vmcnt(0)) -- including the
+// ones issued for later stages, which would drain the pipeline at every
+// barrier.  Each wave instead waits for exactly the copies of the tile it
+// needs (wait_vmcnt) and then meets the others here; the acquire fence keeps
+// the LDS reads that follow from moving above the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 enum : int { kCVec = 1, kDVec = 2, kBiasVec = 4 };
 
@@ -86,15 +113,17 @@ __device__ __forceinline__ void schedule(int bid, int tiles_m, int tiles_n, int&
 }
 
 // ------------------------------------------------------------ fast loader
-// One k-tile slab of ROWS rows x 128 bytes via direct global -> LDS copies.
-// The strip-mined map (ROWS x 8 chunks, 256 threads, one chunk per access)
-// puts thread t of iteration it at LDS slot t + 256*it, which is exactly the
+// One k-tile slab of ROWS rows x kRowBytes bytes via direct global -> LDS
+// copies.  The strip-mined map (ROWS x kChunks chunks, 256 threads, one chunk
+// per access) puts thread t of iteration it at LDS slot t + 256*it, which is the
 // lane-linear slot the DMA writes; the lane fetches the logical chunk that
 // the swizzle assigns to that slot.
-template <int ROWS>
+template <int ROWS, int kRowBytes>
 __device__ __forceinline__ void dma_slab(const uint8_t* __restrict__ base, int64_t row_bytes,
                                          int row0, int rows_valid, int64_t kbyte0, uint8_t* slab,
                                          int tid) {
+  using Swz = typename Slab<kRowBytes>::Swz;
+  constexpr int kChunks = Slab<kRowBytes>::kChunks;
   constexpr StripMinedMap map(ROWS, kChunks, kThreads, 1, ROWS * kChunks / kThreads);
   static_assert(map.well_formed(), "slab thread map");
 #pragma unroll
@@ -108,13 +137,32 @@ __device__ __forceinline__ void dma_slab(const uint8_t* __restrict__ base, int64
   }
 }
 
+// Instruction `it` of dma_slab on its own, so a kernel can spread the copy
+// of a slab between its matrix-core instructions.
+template <int ROWS, int kRowBytes>
+__device__ __forceinline__ void dma_one(const uint8_t* __restrict__ base, int64_t row_bytes,
+                                        int row0, int rows_valid, int64_t kbyte0, uint8_t* slab,
+                                        int tid, int it) {
+  using Swz = typename Slab<kRowBytes>::Swz;
+  constexpr int kChunks = Slab<kRowBytes>::kChunks;
+  constexpr StripMinedMap map(ROWS, kChunks, kThreads, 1, ROWS * kChunks / kThreads);
+  const int r = map.strided(tid, it);
+  const int c = Swz::chunk(r, map.contiguous(tid, 0));
+  const int gr = min(row0 + r, rows_valid - 1);
+  const uint8_t* src = base + gr * row_bytes + kbyte0 + c * 16;
+  uint8_t* dst = slab + map.index(tid & ~63, it, 0) * 16;  // wave-uniform
+  __builtin_amdgcn_global_load_lds(src, to_lds(dst), 16, 0, 0);
+}
+
 // --------------------------------------------------------- general loader
 // Element-predicated, register-staged slab copy for any operand view
 // (row, k) -> row*s_r + k*s_k.  K-contiguous views use the row-contiguous
 // thread map (consecutive lanes walk K); the others use the column-major
 // variant (consecutive lanes walk rows, so each element load coalesces).
-template <int ROWS, int EB>
+template <int ROWS, int EB, int kRowBytes>
 struct RegSlab {
+  using Swz = typename Slab<kRowBytes>::Swz;
+  static constexpr int kChunks = Slab<kRowBytes>::kChunks;
   static constexpr int kI = ROWS * kChunks / kThreads;
   static constexpr int kCE = 16 / EB;  // elements per 16-byte chunk
   i32x4 v[kI];
@@ -169,10 +217,11 @@ struct RegSlab {
 // ------------------------------------------------------- fragment loader
 // Lane l's operand fragment for MFMA k-step ks: row `row` of the slab, the
 // (l/32)-th kLaneBytes-wide half of the step's K bytes.
-template <int kCode>
+template <int kCode, int kRowBytes>
 __device__ __forceinline__ typename MfmaAtom<kCode>::Frag load_frag(const uint8_t* slab, int row,
                                                                    int ks, int lane) {
   using Atom = MfmaAtom<kCode>;
+  using Swz = typename Slab<kRowBytes>::Swz;
   constexpr int kStepBytes = Atom::kK * elem_bytes(kCode);
   const int c0 = (ks * kStepBytes + (lane >> 5) * Atom::kLaneBytes) / 16;
   const uint8_t* rowp = slab + row * kRowBytes;
@@ -264,8 +313,161 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, int m, int n, con
   }
 }
 
+// ------------------------------------------------------------- fast kernel
+// Both operands K-contiguous with 16-byte aligned rows, K a multiple of the
+// slab width.  kStages LDS stages of BM + BN rows x kRowBytes; k-tile kt
+// lives in stage kt % kStages.
+//
+// Schedule (one software pipeline over every MFMA k-step of every tile):
+//  * the direct HBM -> LDS copies of tile kt + kStages - 1 are issued one
+//    instruction at a time between the MFMAs of tile kt, so copy issue never
+//    blocks the matrix cores and each copy has kStages - 2 tiles of MFMA work
+//    to land in;
+//  * the fragments of step g+1 are read from LDS at the start of step g;
+//  * half-way through the last step of tile kt every wave waits for tile
+//    kt+1 and meets at one barrier, which also frees tile kt-1's stage for
+//    the next copy.
+// Past the end of K the copies reload the last k-tile into the free stage,
+// so every tile issues the same number of copies and the wait counts are
+// constants.
+template <int kCode, int BM, int BN, int kRowBytes, int kStages>
+__global__ __launch_bounds__(kThreads) void gemm_fast_kernel(const GemmParams p) {
+  using Atom = MfmaAtom<kCode>;
+  using Frag = typename Atom::Frag;
+  constexpr int EB = elem_bytes(kCode);
+  constexpr int BK = kRowBytes / EB;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int KSTEPS = BK / Atom::kK;
+  static_assert(KSTEPS >= 1 && BK % Atom::kK == 0, "slab narrower than one MFMA step");
+  static_assert(kStages >= 3, "copies need at least one tile of cover");
+  constexpr int SLAB_A = BM * kRowBytes, STAGE = (BM + BN) * kRowBytes;
+  static_assert(kStages * STAGE <= 160 * 1024, "LDS budget");
+  constexpr int kChunks = Slab<kRowBytes>::kChunks;
+  constexpr int IA = BM * kChunks / kThreads, IB = BN * kChunks / kThreads;
+  constexpr int kLoads = IA + IB;                  // copies per thread per tile
+  constexpr int kReads = (FM + FN) * (Atom::kLaneBytes / 16);
+  constexpr int kMfmas = FM * FN;
+  // copies per full step, the rest go into the first half of the last step
+  constexpr int kPerStep = KSTEPS > 1 ? (kLoads + KSTEPS - 1) / KSTEPS : 0;
+  constexpr int kFull = kPerStep * (KSTEPS - 1) < kLoads ? kPerStep * (KSTEPS - 1) : kLoads;
+  constexpr int kLast = kLoads - kFull;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tm, tn;
+  schedule(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm0 = (wave & 1) * WM, wn0 = (wave >> 1) * WN;
+  const int64_t a_rb = p.a_sr * EB, b_rb = p.b_sr * EB;
+  const int KT = p.K / BK;
+
+  f32x16 acc[FM][FN];
+  static_for<FM>([&](auto i) { static_for<FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
+  Frag a[2][FM], b[2][FN];
+  auto read_frags = [&](auto buf, const uint8_t* stage, auto ks) {
+    static_for<FM>([&](auto i) {
+      a[buf][i] = load_frag<kCode, kRowBytes>(stage, wm0 + 32 * i + (lane & 31), ks, lane);
+    });
+    static_for<FN>([&](auto j) {
+      b[buf][j] = load_frag<kCode, kRowBytes>(stage + SLAB_A, wn0 + 32 * j + (lane & 31), ks, lane);
+    });
+  };
+  auto mma = [&](auto buf, auto idx) {
+    Atom::mma(acc[idx / FN][idx % FN], b[buf][idx % FN], a[buf][idx / FN]);
+  };
+  // copy q (0 .. kLoads-1) of tile t into its stage; tiles past K reload the last one
+  auto copy = [&](int t, auto q) {
+    uint8_t* st = smem + (t % kStages) * STAGE;
+    const int64_t kb = (int64_t)min(t, KT - 1) * kRowBytes;
+    if constexpr (q < IA)
+      dma_one<BM, kRowBytes>(p.A, a_rb, m0, p.M, kb, st, tid, q);
+    else
+      dma_one<BN, kRowBytes>(p.B, b_rb, n0, p.N, kb, st + SLAB_A, tid, q - IA);
+  };
+  // MFMAs [lo, hi) of a step with copies [q0, q0 + nq) of tile t spread
+  // evenly between them: after MFMA k come copies [k*nq/n, (k+1)*nq/n).
+  auto mfmas_with_copies = [&](auto buf, auto lo, auto hi, int t, auto q0, auto nq) {
+    constexpr int n = hi - lo;
+    static_for<n>([&](auto k) {
+      mma(buf, std::integral_constant<int, lo + k>{});
+      constexpr int c0 = k * nq / n, c1 = (k + 1) * nq / n;
+      static_for<c1 - c0>([&](auto c) { copy(t, std::integral_constant<int, q0 + c0 + c>{}); });
+    });
+    static_for<n>([&](auto k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      constexpr int c0 = k * nq / n, c1 = (k + 1) * nq / n;
+      if constexpr (c1 > c0) __builtin_amdgcn_sched_group_barrier(0x020, c1 - c0, 0);
+    });
+  };
+  constexpr int kWait = (kStages - 2) * kLoads;  // copies allowed in flight past the next tile
+
+  auto tile = [&](int kt, auto parity) {
+    const uint8_t* stage = smem + (kt % kStages) * STAGE;
+    const int ct = kt + kStages - 1;  // tile whose copies are issued now
+    static_for<KSTEPS>([&](auto ks) {
+      constexpr int cur = (parity + ks) & 1;
+      if constexpr (ks + 1 < KSTEPS) {
+        read_frags(std::integral_constant<int, cur ^ 1>{}, stage, std::integral_constant<int, ks + 1>{});
+        __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+        constexpr int q0 = ks * kPerStep < kFull ? ks * kPerStep : kFull;
+        constexpr int q1 = (ks + 1) * kPerStep < kFull ? (ks + 1) * kPerStep : kFull;
+        mfmas_with_copies(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
+                          std::integral_constant<int, kMfmas>{}, ct,
+                          std::integral_constant<int, q0>{}, std::integral_constant<int, q1 - q0>{});
+      } else {
+        mfmas_with_copies(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
+                          std::integral_constant<int, kMfmas / 2>{}, ct,
+                          std::integral_constant<int, kFull>{}, std::integral_constant<int, kLast>{});
+        if (kt + 1 < KT) {
+          wait_vmcnt<kWait>();  // tile kt+1 landed (this thread's copies)
+          stage_barrier();      // ... everyone's; tile kt-1's stage is free
+          read_frags(std::integral_constant<int, cur ^ 1>{}, smem + ((kt + 1) % kStages) * STAGE,
+                     std::integral_constant<int, 0>{});
+        }
+        static_for<kMfmas - kMfmas / 2>([&](auto k) {
+          mma(std::integral_constant<int, cur>{}, std::integral_constant<int, kMfmas / 2 + k>{});
+        });
+      }
+    });
+  };
+
+  if (KT > 0) {
+    static_for<kStages - 1>([&](auto t) {
+      static_for<kLoads>([&](auto q) { copy(t, q); });
+    });
+    wait_vmcnt<kWait>();
+    stage_barrier();
+    read_frags(std::integral_constant<int, 0>{}, smem, std::integral_constant<int, 0>{});
+    if constexpr (KSTEPS % 2 == 0) {
+      for (int kt = 0; kt < KT; ++kt) tile(kt, std::integral_constant<int, 0>{});
+    } else {
+      for (int kt = 0; kt < KT; kt += 2) {
+        tile(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < KT) tile(kt + 1, std::integral_constant<int, 1>{});
+      }
+    }
+    wait_vmcnt<0>();  // no copy may land in LDS after the workgroup ends
+  }
+
+  static_for<FM>([&](auto i) {
+    const int m = m0 + wm0 + 32 * i + mfma32_acc_col(lane, 0);
+    static_for<FN>([&](auto j) {
+      static_for<4>([&](auto g) {
+        const int n = n0 + wn0 + 32 * j + mfma32_acc_row(lane, 4 * g);
+        const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                            acc[i][j][4 * g + 3]};
+        epilogue4(p, m, n, v);
+      });
+    });
+  });
+}
+
 // ------------------------------------------------------------------ kernel
-template <int kCode, int BM, int BN, bool kFast>
+// kStages LDS stages of BM + BN rows of kRowBytes bytes each.  K-tile kt
+// lives in stage kt % kStages; up to kStages - 1 tiles are in flight, so the
+// copy of a tile has kStages - 1 tiles of matrix-core work to arrive in.
+template <int kCode, int BM, int BN, int kRowBytes, int kStages, bool kFast>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   using Atom = MfmaAtom<kCode>;
   using Frag = typename Atom::Frag;
@@ -274,8 +476,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   constexpr int WM = BM / 2, WN = BN / 2;    // 2 x 2 wavefronts
   constexpr int FM = WM / 32, FN = WN / 32;  // MFMA tiles per wave
   constexpr int KSTEPS = BK / Atom::kK;
+  static_assert(KSTEPS >= 1 && BK % Atom::kK == 0, "slab narrower than one MFMA step");
   constexpr int SLAB_A = BM * kRowBytes, STAGE = (BM + BN) * kRowBytes;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  static_assert(kStages * STAGE <= 160 * 1024, "LDS budget");
+  // global_load_lds instructions one thread issues per k-tile
+  constexpr int kLoadsPerTile = (BM + BN) * kRowBytes / 16 / kThreads;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tm, tn;
@@ -286,59 +492,100 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   f32x16 acc[FM][FN];
   static_for<FM>([&](auto i) { static_for<FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
 
-  // One k-tile from LDS: the fragments of MFMA k-step ks+1 are read while
-  // the MFMAs of step ks run (two fragment buffers), so LDS latency hides
-  // behind matrix-core work.
-  auto compute = [&](const uint8_t* stage) {
-    const uint8_t* sa = stage;
-    const uint8_t* sb = stage + SLAB_A;
-    Frag a[2][FM], b[2][FN];
-    auto load = [&](auto buf, auto ks) {
-      static_for<FM>([&](auto i) { a[buf][i] = load_frag<kCode>(sa, wm0 + 32 * i + (lane & 31), ks, lane); });
-      static_for<FN>([&](auto j) { b[buf][j] = load_frag<kCode>(sb, wn0 + 32 * j + (lane & 31), ks, lane); });
-    };
-    load(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    static_for<KSTEPS>([&](auto ks) {
-      constexpr int cur = ks & 1;
-      if constexpr (ks + 1 < KSTEPS) load(std::integral_constant<int, cur ^ 1>{}, std::integral_constant<int, ks + 1>{});
-      static_for<FM>([&](auto i) { static_for<FN>([&](auto j) { Atom::mma(acc[i][j], b[cur][j], a[cur][i]); }); });
+  // Fragment double buffer and the pieces of one MFMA k-step.
+  Frag a[2][FM], b[2][FN];
+  auto read_frags = [&](auto buf, const uint8_t* stage, auto ks) {
+    static_for<FM>([&](auto i) {
+      a[buf][i] = load_frag<kCode, kRowBytes>(stage, wm0 + 32 * i + (lane & 31), ks, lane);
     });
-    // Instruction order for the scheduler: the first step's fragment reads,
-    // then for each step its MFMAs interleaved with the next step's reads.
-    constexpr int kReads = (FM + FN) * (Atom::kLaneBytes / 16);
-    constexpr int kMfmas = FM * FN;
-    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-    static_for<KSTEPS - 1>([&](auto) {
-      static_for<kReads>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas / kReads > 0 ? kMfmas / kReads : 1, 0);
-      });
+    static_for<FN>([&](auto j) {
+      b[buf][j] = load_frag<kCode, kRowBytes>(stage + SLAB_A, wn0 + 32 * j + (lane & 31), ks, lane);
     });
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfmas, 0);
   };
+  // MFMAs number lo .. hi-1 of a step (i major, j minor)
+  auto mfmas = [&](auto buf, auto lo, auto hi) {
+    static_for<hi - lo>([&](auto q) {
+      constexpr int idx = lo + q;
+      Atom::mma(acc[idx / FN][idx % FN], b[buf][idx % FN], a[buf][idx / FN]);
+    });
+  };
+  constexpr int kReads = (FM + FN) * (Atom::kLaneBytes / 16);
+  constexpr int kMfmas = FM * FN;
 
   const int KT = (p.K + BK - 1) / BK;
   if constexpr (kFast) {
+    // One software pipeline over all k-steps.  The fragments of step g+1 are
+    // read at the start of step g, a whole step of MFMAs before use.  In the
+    // last step of k-tile kt, half-way through its MFMAs, every wave waits
+    // for tile kt+1 and meets at a barrier; that barrier also proves every
+    // wave is done reading tile kt's stage, which is refilled at once with
+    // tile kt+kStages.
+    static_assert(KSTEPS % 2 == 0, "fragment buffers alternate per step");
     const int64_t a_rb = p.a_sr * EB, b_rb = p.b_sr * EB;
+    auto issue = [&](int kt) {
+      uint8_t* st = smem + (kt % kStages) * STAGE;
+      const int64_t kb = (int64_t)kt * kRowBytes;
+      dma_slab<BM, kRowBytes>(p.A, a_rb, m0, p.M, kb, st, tid);
+      dma_slab<BN, kRowBytes>(p.B, b_rb, n0, p.N, kb, st + SLAB_A, tid);
+    };
+    // wait until tile `t` has landed, given tiles up to `last_issued` were issued
+    auto wait_tile = [&](int t, int last_issued) {
+      const int after = min(kStages - 1, last_issued - t);
+      static_for<kStages>([&](auto n) {
+        if (after == n) wait_vmcnt<n * kLoadsPerTile>();
+      });
+    };
+    static_for<kStages>([&](auto s) {
+      if (s < KT) issue(s);
+    });
     if (KT > 0) {
-      dma_slab<BM>(p.A, a_rb, m0, p.M, 0, smem, tid);
-      dma_slab<BN>(p.B, b_rb, n0, p.N, 0, smem + SLAB_A, tid);
+      wait_tile(0, min(kStages, KT) - 1);
+      __syncthreads();
+      read_frags(std::integral_constant<int, 0>{}, smem, std::integral_constant<int, 0>{});
     }
     for (int kt = 0; kt < KT; ++kt) {
-      uint8_t* cur = smem + (kt & 1) * STAGE;
-      uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's copies of k-tile kt landed
-      __syncthreads();                     // ... and everyone's; stage nxt is no longer read
-      if (kt + 1 < KT) {
-        const int64_t kb = (int64_t)(kt + 1) * kRowBytes;
-        dma_slab<BM>(p.A, a_rb, m0, p.M, kb, nxt, tid);
-        dma_slab<BN>(p.B, b_rb, n0, p.N, kb, nxt + SLAB_A, tid);
-      }
-      compute(cur);
+      const uint8_t* stage = smem + (kt % kStages) * STAGE;
+      static_for<KSTEPS>([&](auto ks) {
+        constexpr int cur = ks & 1;
+        if constexpr (ks + 1 < KSTEPS) {
+          read_frags(std::integral_constant<int, cur ^ 1>{}, stage,
+                     std::integral_constant<int, ks + 1>{});
+          mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
+                std::integral_constant<int, kMfmas>{});
+          __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, kMfmas, 0);
+        } else {
+          mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
+                std::integral_constant<int, kMfmas / 2>{});
+          if (kt + 1 < KT) {
+            // tiles issued so far: 0 .. min(kt + kStages - 1, KT - 1)
+            wait_tile(kt + 1, min(kt + kStages - 1, KT - 1));
+            __syncthreads();
+            if (kt + kStages < KT) issue(kt + kStages);
+            read_frags(std::integral_constant<int, cur ^ 1>{},
+                       smem + ((kt + 1) % kStages) * STAGE, std::integral_constant<int, 0>{});
+          }
+          mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, kMfmas / 2>{},
+                std::integral_constant<int, kMfmas>{});
+        }
+      });
     }
   } else {
-    RegSlab<BM, EB> ra;
-    RegSlab<BN, EB> rb;
+    static_assert(kStages == 2, "register-staged path double-buffers");
+    // k-steps of one tile from LDS, fragments of step ks+1 read during ks
+    auto compute = [&](const uint8_t* stage) {
+      read_frags(std::integral_constant<int, 0>{}, stage, std::integral_constant<int, 0>{});
+      static_for<KSTEPS>([&](auto ks) {
+        constexpr int cur = ks & 1;
+        if constexpr (ks + 1 < KSTEPS)
+          read_frags(std::integral_constant<int, cur ^ 1>{}, stage,
+                     std::integral_constant<int, ks + 1>{});
+        mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
+              std::integral_constant<int, kMfmas>{});
+      });
+    };
+    RegSlab<BM, EB, kRowBytes> ra;
+    RegSlab<BN, EB, kRowBytes> rb;
     const bool a_vec = (p.flags >> 8) & 1, b_vec = (p.flags >> 9) & 1;
     const bool a_kc = (p.a_sk == 1), b_kc = (p.b_sk == 1);
     if (KT > 0) {
@@ -381,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 }
 
 // ----------------------------------------------------------------- dispatch
-template <int kCode, int BM, int BN, bool kFast>
+template <int kCode, int BM, int BN, int kRowBytes, int kStages, bool kFast>
 int launch(const GemmParams& p0, hipStream_t stream) {
   GemmParams p = p0;
   p.tiles_m = (p.M + BM - 1) / BM;
@@ -389,25 +636,43 @@ int launch(const GemmParams& p0, hipStream_t stream) {
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
   if (grid <= 0) return TLA_OK;
   if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((gemm_kernel<kCode, BM, BN, kFast>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     stream, p);
+  if constexpr (kFast && kStages >= 3)
+    hipLaunchKernelGGL((gemm_fast_kernel<kCode, BM, BN, kRowBytes, kStages>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_kernel<kCode, BM, BN, kRowBytes, kStages, kFast>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
 }
 
 bool aligned(const void* p, int64_t bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
 
+// The variants the library ships.  16-bit operands: the interleaved-copy
+// kernel with 64-byte slabs in 4 stages.  e4m3 (whose 32-byte fragments leave
+// no registers for a second buffer set in that kernel): the two-stage kernel
+// with 128-byte slabs.  The fast variants need K to be a multiple of their
+// slab width; fast_slab_bytes() says which.
 template <int kCode>
-int dispatch_typed(const GemmProblem& g, const GemmParams& p, bool fast, bool big, hipStream_t s,
-                   bool dry, const char** name) {
-  static const char* names[4] = {"gemm_fast_256x256", "gemm_fast_128x128", "gemm_general_128x128",
-                                 "gemm_general_128x128"};
+struct FastConfig {
+  static constexpr int kRowBytes = kCode == kE4M3 ? 128 : 64;
+  static constexpr int kStages = kCode == kE4M3 ? 2 : 4;
+};
+
+int fast_slab_bytes(int code) {
+  return code == kE4M3 ? FastConfig<kE4M3>::kRowBytes : FastConfig<kBF16>::kRowBytes;
+}
+
+template <int kCode>
+int dispatch_typed(const GemmParams& p, bool fast, bool big, hipStream_t s, bool dry,
+                   const char** name) {
+  using F = FastConfig<kCode>;
+  static const char* names[3] = {"gemm_fast_256x256", "gemm_fast_128x128", "gemm_general_128x128"};
   const int v = fast ? (big ? 0 : 1) : 2;
   if (name) *name = names[v];
   if (dry) return TLA_OK;
-  (void)g;
-  if (v == 0) return launch<kCode, 256, 256, true>(p, s);
-  if (v == 1) return launch<kCode, 128, 128, true>(p, s);
-  return launch<kCode, 128, 128, false>(p, s);
+  if (v == 0) return launch<kCode, 256, 256, F::kRowBytes, F::kStages, true>(p, s);
+  if (v == 1) return launch<kCode, 128, 128, F::kRowBytes, F::kStages, true>(p, s);
+  return launch<kCode, 128, 128, 128, 2, false>(p, s);
 }
 
 }  // namespace
@@ -447,14 +712,14 @@ int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const 
   const bool a_vec = (g.a_order == TLA_ROW_MAJOR) && ((g.lda * eb) % 16 == 0) && aligned(g.A, 16);
   const bool b_vec = (g.b_order == TLA_COL_MAJOR) && ((g.ldb * eb) % 16 == 0) && aligned(g.B, 16);
   p.flags |= (a_vec ? 1 << 8 : 0) | (b_vec ? 1 << 9 : 0);
-  const int BK = kRowBytes / eb;
+  const int BK = fast_slab_bytes(g.a_type) / eb;
   const bool fast = a_vec && b_vec && g.K > 0 && (g.K % BK) == 0;
   const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256);
   const bool big = tiles256 >= 128;
   switch (g.a_type) {
-    case TLA_BF16: return dispatch_typed<kBF16>(g, p, fast, big, stream, dry_run, name);
-    case TLA_F16: return dispatch_typed<kF16>(g, p, fast, big, stream, dry_run, name);
-    case TLA_E4M3: return dispatch_typed<kE4M3>(g, p, fast, big, stream, dry_run, name);
+    case TLA_BF16: return dispatch_typed<kBF16>(p, fast, big, stream, dry_run, name);
+    case TLA_F16: return dispatch_typed<kF16>(p, fast, big, stream, dry_run, name);
+    case TLA_E4M3: return dispatch_typed<kE4M3>(p, fast, big, stream, dry_run, name);
     default: return TLA_ERR_UNSUPPORTED;
   }
 }
