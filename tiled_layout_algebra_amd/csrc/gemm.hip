@@ -139,13 +139,13 @@ __device__ __forceinline__ void dma_slab(const uint8_t* __restrict__ base, int64
 
 // Instruction `it` of dma_slab on its own, so a kernel can spread the copy
 // of a slab between its matrix-core instructions.
-template <int ROWS, int kRowBytes>
+template <int ROWS, int kRowBytes, int NT = kThreads>
 __device__ __forceinline__ void dma_one(const uint8_t* __restrict__ base, int64_t row_bytes,
                                         int row0, int rows_valid, int64_t kbyte0, uint8_t* slab,
                                         int tid, int it) {
   using Swz = typename Slab<kRowBytes>::Swz;
   constexpr int kChunks = Slab<kRowBytes>::kChunks;
-  constexpr StripMinedMap map(ROWS, kChunks, kThreads, 1, ROWS * kChunks / kThreads);
+  constexpr StripMinedMap map(ROWS, kChunks, NT, 1, ROWS * kChunks / NT);
   const int r = map.strided(tid, it);
   const int c = Swz::chunk(r, map.contiguous(tid, 0));
   const int gr = min(row0 + r, rows_valid - 1);
@@ -313,6 +313,78 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, int m, int n, con
   }
 }
 
+// The epilogue of one wavefront's FM x FN grid of 32x32 accumulator tiles,
+// rows m_base + 32i + lane%32, column groups n_base + 32j + 8g + 4(lane/32).
+// When the whole wave tile lies inside D and every access can be an aligned
+// 8-byte vector (16-bit C, D and bias), all C and bias loads are issued first
+// and only then is the arithmetic done and D stored, so the wave pays the
+// global-memory latency once instead of once per group.  Otherwise each group
+// of four columns goes through the predicated epilogue4.
+template <int FM, int FN>
+__device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, int n_base, int lane,
+                                               f32x16 (&acc)[FM][FN]) {
+  const bool full = m_base + 32 * FM <= p.M && n_base + 32 * FN <= p.N;
+  const bool c_vec = p.beta == 0.f || ((p.flags & kCVec) && p.c_type != kF32);
+  const bool b_vec = !p.bias || ((p.flags & kBiasVec) && p.bias_type != kF32);
+  if (full && c_vec && b_vec && (p.flags & kDVec)) {
+    const int row = lane & 31, half = lane >> 5;
+    float bias[FN][4][4];
+    static_for<FN>([&](auto j) {
+      static_for<4>([&](auto g) {
+        static_for<4>([&](auto q) { bias[j][g][q] = 0.f; });
+        if (p.bias) load4(p.bias, p.bias_type, n_base + 32 * j + 8 * g + 4 * half, bias[j][g]);
+      });
+    });
+    uint2 c[FM][FN][4];
+    if (p.beta != 0.f) {
+      const uint16_t* C = (const uint16_t*)p.C;
+      static_for<FM>([&](auto i) {
+        static_for<FN>([&](auto j) {
+          static_for<4>([&](auto g) {
+            c[i][j][g] = *(const uint2*)(C + (int64_t)(m_base + 32 * i + row) * p.c_sm + n_base +
+                                         32 * j + 8 * g + 4 * half);
+          });
+        });
+      });
+    }
+    uint16_t* D = (uint16_t*)p.D;
+    static_for<FM>([&](auto i) {
+      static_for<FN>([&](auto j) {
+        static_for<4>([&](auto g) {
+          float y[4];
+          static_for<4>([&](auto q) { y[q] = p.alpha * acc[i][j][4 * g + q]; });
+          if (p.beta != 0.f) {
+            const uint32_t w[4] = {c[i][j][g].x & 0xFFFFu, c[i][j][g].x >> 16, c[i][j][g].y & 0xFFFFu,
+                                   c[i][j][g].y >> 16};
+            static_for<4>([&](auto q) {
+              const float cv = p.c_type == kBF16 ? __builtin_bit_cast(float, w[q] << 16)
+                                                 : (float)__builtin_bit_cast(_Float16, (uint16_t)w[q]);
+              y[q] += p.beta * cv;
+            });
+          }
+          static_for<4>([&](auto q) { y[q] = activate(y[q] + bias[j][g][q], p.act); });
+          uint2 u;
+          u.x = (uint32_t)to_bits(y[0], p.d_type) | ((uint32_t)to_bits(y[1], p.d_type) << 16);
+          u.y = (uint32_t)to_bits(y[2], p.d_type) | ((uint32_t)to_bits(y[3], p.d_type) << 16);
+          *(uint2*)(D + (int64_t)(m_base + 32 * i + row) * p.d_sm + n_base + 32 * j + 8 * g + 4 * half) = u;
+        });
+      });
+    });
+  } else {
+    static_for<FM>([&](auto i) {
+      const int m = m_base + 32 * i + mfma32_acc_col(lane, 0);
+      static_for<FN>([&](auto j) {
+        static_for<4>([&](auto g) {
+          const int n = n_base + 32 * j + mfma32_acc_row(lane, 4 * g);
+          const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                              acc[i][j][4 * g + 3]};
+          epilogue4(p, m, n, v);
+        });
+      });
+    });
+  }
+}
+
 // ------------------------------------------------------------- fast kernel
 // Both operands K-contiguous with 16-byte aligned rows, K a multiple of the
 // slab width.  kStages LDS stages of BM + BN rows x kRowBytes; k-tile kt
@@ -330,26 +402,31 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, int m, int n, con
 // Past the end of K the copies reload the last k-tile into the free stage,
 // so every tile issues the same number of copies and the wait counts are
 // constants.
-template <int kCode, int BM, int BN, int kRowBytes, int kStages>
-__global__ __launch_bounds__(kThreads) void gemm_fast_kernel(const GemmParams p) {
+template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront = 0, int kWM = 2,
+          int kWN = 2>
+__global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmParams p) {
   using Atom = MfmaAtom<kCode>;
   using Frag = typename Atom::Frag;
+  constexpr int NT = 64 * kWM * kWN;  // kWM x kWN wavefronts
   constexpr int EB = elem_bytes(kCode);
   constexpr int BK = kRowBytes / EB;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / kWM, WN = BN / kWN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int KSTEPS = BK / Atom::kK;
   static_assert(KSTEPS >= 1 && BK % Atom::kK == 0, "slab narrower than one MFMA step");
-  static_assert(kStages >= 3, "copies need at least one tile of cover");
+  static_assert(kStages >= 2, "copies need a free stage");
   constexpr int SLAB_A = BM * kRowBytes, STAGE = (BM + BN) * kRowBytes;
   static_assert(kStages * STAGE <= 160 * 1024, "LDS budget");
   constexpr int kChunks = Slab<kRowBytes>::kChunks;
-  constexpr int IA = BM * kChunks / kThreads, IB = BN * kChunks / kThreads;
+  constexpr int IA = BM * kChunks / NT, IB = BN * kChunks / NT;
   constexpr int kLoads = IA + IB;                  // copies per thread per tile
   constexpr int kReads = (FM + FN) * (Atom::kLaneBytes / 16);
   constexpr int kMfmas = FM * FN;
-  // copies per full step, the rest go into the first half of the last step
-  constexpr int kPerStep = KSTEPS > 1 ? (kLoads + KSTEPS - 1) / KSTEPS : 0;
+  // Copies per full step, the rest go into the first half of the last step.
+  // kFront > 0 puts all copies into the first kFront steps instead (as early
+  // as possible, for shallow pipelines).
+  constexpr int kSpread = kFront > 0 && kFront < KSTEPS ? kFront : KSTEPS;
+  constexpr int kPerStep = KSTEPS > 1 ? (kLoads + kSpread - 1) / kSpread : 0;
   constexpr int kFull = kPerStep * (KSTEPS - 1) < kLoads ? kPerStep * (KSTEPS - 1) : kLoads;
   constexpr int kLast = kLoads - kFull;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * STAGE];
@@ -358,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fast_kernel(const GemmParams p)
   int tm, tn;
   schedule(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int wm0 = (wave & 1) * WM, wn0 = (wave >> 1) * WN;
+  const int wm0 = (wave % kWM) * WM, wn0 = (wave / kWM) * WN;
   const int64_t a_rb = p.a_sr * EB, b_rb = p.b_sr * EB;
   const int KT = p.K / BK;
 
@@ -381,9 +458,9 @@ __global__ __launch_bounds__(kThreads) void gemm_fast_kernel(const GemmParams p)
     uint8_t* st = smem + (t % kStages) * STAGE;
     const int64_t kb = (int64_t)min(t, KT - 1) * kRowBytes;
     if constexpr (q < IA)
-      dma_one<BM, kRowBytes>(p.A, a_rb, m0, p.M, kb, st, tid, q);
+      dma_one<BM, kRowBytes, NT>(p.A, a_rb, m0, p.M, kb, st, tid, q);
     else
-      dma_one<BN, kRowBytes>(p.B, b_rb, n0, p.N, kb, st + SLAB_A, tid, q - IA);
+      dma_one<BN, kRowBytes, NT>(p.B, b_rb, n0, p.N, kb, st + SLAB_A, tid, q - IA);
   };
   // MFMAs [lo, hi) of a step with copies [q0, q0 + nq) of tile t spread
   // evenly between them: after MFMA k come copies [k*nq/n, (k+1)*nq/n).
@@ -450,17 +527,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fast_kernel(const GemmParams p)
     wait_vmcnt<0>();  // no copy may land in LDS after the workgroup ends
   }
 
-  static_for<FM>([&](auto i) {
-    const int m = m0 + wm0 + 32 * i + mfma32_acc_col(lane, 0);
-    static_for<FN>([&](auto j) {
-      static_for<4>([&](auto g) {
-        const int n = n0 + wn0 + 32 * j + mfma32_acc_row(lane, 4 * g);
-        const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                            acc[i][j][4 * g + 3]};
-        epilogue4(p, m, n, v);
-      });
-    });
-  });
+  epilogue_tiles<FM, FN>(p, m0 + wm0, n0 + wn0, lane, acc);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -614,65 +681,68 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   // Epilogue: acc[i][j] holds the D^T piece for rows m0+wm0+32i.. and
   // columns n0+wn0+32j..; value r of lane l sits at (row, col) =
   // (lane%32, mfma32_acc_row(l, r)) of that 32x32 piece.
-  static_for<FM>([&](auto i) {
-    const int m = m0 + wm0 + 32 * i + mfma32_acc_col(lane, 0);
-    static_for<FN>([&](auto j) {
-      static_for<4>([&](auto g) {
-        const int n = n0 + wn0 + 32 * j + mfma32_acc_row(lane, 4 * g);
-        const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                            acc[i][j][4 * g + 3]};
-        epilogue4(p, m, n, v);
-      });
-    });
-  });
+  epilogue_tiles<FM, FN>(p, m0 + wm0, n0 + wn0, lane, acc);
 }
 
 // ----------------------------------------------------------------- dispatch
-template <int kCode, int BM, int BN, int kRowBytes, int kStages, bool kFast>
-int launch(const GemmParams& p0, hipStream_t stream) {
-  GemmParams p = p0;
+bool aligned(const void* p, int64_t bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
+
+void set_grid(GemmParams& p, int BM, int BN, int64_t* grid) {
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
-  const int64_t grid = (int64_t)p.tiles_m * p.tiles_n;
+  *grid = (int64_t)p.tiles_m * p.tiles_n;
+}
+
+template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront, int kWM, int kWN>
+int launch_fast(const GemmParams& p0, hipStream_t stream) {
+  GemmParams p = p0;
+  int64_t grid;
+  set_grid(p, BM, BN, &grid);
   if (grid <= 0) return TLA_OK;
   if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
-  if constexpr (kFast && kStages >= 3)
-    hipLaunchKernelGGL((gemm_fast_kernel<kCode, BM, BN, kRowBytes, kStages>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm_kernel<kCode, BM, BN, kRowBytes, kStages, kFast>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((gemm_fast_kernel<kCode, BM, BN, kRowBytes, kStages, kFront, kWM, kWN>),
+                     dim3((unsigned)grid), dim3(64 * kWM * kWN), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
 }
 
-bool aligned(const void* p, int64_t bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
-
-// The variants the library ships.  16-bit operands: the interleaved-copy
-// kernel with 64-byte slabs in 4 stages.  e4m3 (whose 32-byte fragments leave
-// no registers for a second buffer set in that kernel): the two-stage kernel
-// with 128-byte slabs.  The fast variants need K to be a multiple of their
-// slab width; fast_slab_bytes() says which.
-template <int kCode>
-struct FastConfig {
-  static constexpr int kRowBytes = kCode == kE4M3 ? 128 : 64;
-  static constexpr int kStages = kCode == kE4M3 ? 2 : 4;
-};
-
-int fast_slab_bytes(int code) {
-  return code == kE4M3 ? FastConfig<kE4M3>::kRowBytes : FastConfig<kBF16>::kRowBytes;
+template <int kCode, int BM, int BN, int kRowBytes, bool kFast>
+int launch_two_stage(const GemmParams& p0, hipStream_t stream) {
+  GemmParams p = p0;
+  int64_t grid;
+  set_grid(p, BM, BN, &grid);
+  if (grid <= 0) return TLA_OK;
+  if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((gemm_kernel<kCode, BM, BN, kRowBytes, 2, kFast>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
 }
+
+// The variants the library ships.  Every fast variant moves whole 128-byte
+// K rows per copy (the direct-to-LDS copy rate per compute unit halves with
+// every halving of the row width), so K must be a multiple of 128 bytes.
+//   16-bit, >= 128 tiles of 256x256: 8 wavefronts (2x4, 128x64 each), two
+//     stages, each tile's copies issued during the first two MFMA steps of
+//     the tile before.
+//   16-bit, smaller: 128x128, 4 wavefronts, three stages.
+//   e4m3: the two-stage kernel (its 32-byte fragments do not fit the
+//     8-wavefront register budget).
+int fast_slab_bytes(int) { return 128; }
 
 template <int kCode>
 int dispatch_typed(const GemmParams& p, bool fast, bool big, hipStream_t s, bool dry,
                    const char** name) {
-  using F = FastConfig<kCode>;
   static const char* names[3] = {"gemm_fast_256x256", "gemm_fast_128x128", "gemm_general_128x128"};
   const int v = fast ? (big ? 0 : 1) : 2;
   if (name) *name = names[v];
   if (dry) return TLA_OK;
-  if (v == 0) return launch<kCode, 256, 256, F::kRowBytes, F::kStages, true>(p, s);
-  if (v == 1) return launch<kCode, 128, 128, F::kRowBytes, F::kStages, true>(p, s);
-  return launch<kCode, 128, 128, 128, 2, false>(p, s);
+  if constexpr (kCode == kE4M3) {
+    if (v == 0) return launch_two_stage<kCode, 256, 256, 128, true>(p, s);
+    if (v == 1) return launch_two_stage<kCode, 128, 128, 128, true>(p, s);
+  } else {
+    if (v == 0) return launch_fast<kCode, 256, 256, 128, 2, 2, 2, 4>(p, s);
+    if (v == 1) return launch_fast<kCode, 128, 128, 128, 3, 1, 2, 2>(p, s);
+  }
+  return launch_two_stage<kCode, 128, 128, 128, false>(p, s);
 }
 
 }  // namespace
