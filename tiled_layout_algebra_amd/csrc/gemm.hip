@@ -12,7 +12,8 @@
 // current one feeds the matrix cores (section 四: pipeline stages hide global
 // latency).  The epilogue applies alpha, beta*C, bias and the activation to
 // the fp32 accumulators in registers and stores D once (section 四: fuse
-// before the store).
+// before the store); for whole tiles the freed LDS stages turn C and D into
+// whole-row transfers (see epilogue_lds).
 //
 // Operand roles.  Both LDS slabs hold rows of K (A by m, B by n).  The MFMA
 // is issued with the B rows as its first operand and the A rows as its
@@ -72,7 +73,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-enum : int { kCVec = 1, kDVec = 2, kBiasVec = 4 };
+// p.flags: C / D / bias rows allow aligned 4-element (8-byte for 16-bit)
+// vectors; C / D rows (16-bit) allow aligned 16-byte vectors.
+enum : int { kCVec = 1, kDVec = 2, kBiasVec = 4, kC16 = 8, kD16 = 16 };
 
 struct GemmParams {
   const uint8_t* A;
@@ -313,63 +316,197 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, int m, int n, con
   }
 }
 
-// The epilogue of one wavefront's FM x FN grid of 32x32 accumulator tiles,
-// rows m_base + 32i + lane%32, column groups n_base + 32j + 8g + 4(lane/32).
-// When the whole wave tile lies inside D and every access can be an aligned
-// 8-byte vector (16-bit C, D and bias), all C and bias loads are issued first
-// and only then is the arithmetic done and D stored, so the wave pays the
-// global-memory latency once instead of once per group.  Otherwise each group
-// of four columns goes through the predicated epilogue4.
-template <int FM, int FN>
-__device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, int n_base, int lane,
-                                               f32x16 (&acc)[FM][FN]) {
-  const bool full = m_base + 32 * FM <= p.M && n_base + 32 * FN <= p.N;
-  const bool c_vec = p.beta == 0.f || ((p.flags & kCVec) && p.c_type != kF32);
-  const bool b_vec = !p.bias || ((p.flags & kBiasVec) && p.bias_type != kF32);
-  if (full && c_vec && b_vec && (p.flags & kDVec)) {
-    const int row = lane & 31, half = lane >> 5;
-    float bias[FN][4][4];
+// ------------------------------------------- specialised full-tile epilogue
+// The two fast epilogue paths below are compiled once per activation and
+// per D type, so the per-element work is straight-line code; C and bias
+// (bf16 or fp16) are widened with a select rather than a branch.
+__device__ __forceinline__ float widen16(uint32_t w, bool bf16) {
+  const float b = __builtin_bit_cast(float, w << 16);
+  const float h = (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+  return bf16 ? b : h;
+}
+
+template <int kAct>
+__device__ __forceinline__ float act_t(float y) {
+  if constexpr (kAct == TLA_ACT_RELU) return y > 0.f ? y : 0.f;
+  if constexpr (kAct == TLA_ACT_GELU) return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f));
+  return y;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (kBf16)
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+  else
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+// y = act(alpha*acc + beta*c + bias) for the four values of group g of tile
+// (i, j); c and bias arrive as packed 16-bit pairs.
+template <int kAct, bool kDBf16>
+__device__ __forceinline__ uint2 epi_group(const f32x16& acc, int g, uint2 c, uint2 b, float alpha,
+                                           float beta, bool c_bf16, bool b_bf16) {
+  const uint32_t cw[4] = {c.x, c.x >> 16, c.y, c.y >> 16};
+  const uint32_t bw[4] = {b.x, b.x >> 16, b.y, b.y >> 16};
+  float y[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float v = alpha * acc[4 * g + q];
+    v += beta * widen16(cw[q] & 0xFFFFu, c_bf16);
+    y[q] = act_t<kAct>(v + widen16(bw[q] & 0xFFFFu, b_bf16));
+  }
+  return uint2{pack2<kDBf16>(y[0], y[1]), pack2<kDBf16>(y[2], y[3])};
+}
+
+// This lane's 16-bit bias values for its column groups, all loads issued
+// before any is used (zero bits when there is no bias).
+template <int FN>
+__device__ __forceinline__ void load_bias16(const GemmParams& p, int n_base, int half,
+                                            uint2 (&braw)[FN][4]) {
+  static_for<FN>([&](auto j) { static_for<4>([&](auto g) { braw[j][g] = uint2{0u, 0u}; }); });
+  if (p.bias) {
+    const uint2* b = (const uint2*)((const uint16_t*)p.bias + n_base + 4 * half);
+    static_for<FN>([&](auto j) { static_for<4>([&](auto g) { braw[j][g] = b[8 * j + 2 * g]; }); });
+  }
+}
+
+// Full wave tile through LDS.  In the MFMA result layout a lane holds four
+// consecutive columns of one row, so a direct global access touches 32 rows
+// 16 bytes at a time.  Instead the wave copies its C sub-tile (WM rows of
+// 64*FN bytes) into its own LDS region with whole-row direct copies, applies
+// the epilogue reading C there in the MFMA layout, writes the 16-bit result
+// back in place and stores D from LDS as whole rows.  The region's 16-byte
+// chunks are XOR-swizzled by row so that the lane-per-row accesses of one
+// instruction fall into distinct LDS banks.
+template <int kAct, bool kDBf16, int FM, int FN>
+__device__ __forceinline__ void epilogue_lds(const GemmParams& p, int m_base, int n_base, int lane,
+                                             const f32x16 (&acc)[FM][FN], uint8_t* region) {
+  constexpr int kRowB = 64 * FN, kCh = kRowB / 16, kRowsPerKiB = 1024 / kRowB;
+  static_assert(kCh == 4 || kCh == 8 || kCh == 16, "row width");
+  constexpr int kIters = 32 * FM * kRowB / 1024;
+  auto swz = [](int r, int c) { return c ^ ((r / (16 / kCh)) & (kCh - 1)); };
+  const int row = lane & 31, half = lane >> 5;
+  const int rr = lane / kCh, cs = lane % kCh;  // row-wise view of one KiB
+  const bool has_c = p.beta != 0.f;
+  if (has_c) {
+    const uint8_t* C = p.C + ((int64_t)m_base * p.c_sm + n_base) * 2;
+    static_for<kIters>([&](auto t) {
+      const int r = kRowsPerKiB * t + rr;
+      const uint8_t* src = C + (int64_t)r * p.c_sm * 2 + swz(r, cs) * 16;
+      __builtin_amdgcn_global_load_lds(src, to_lds(region + t * 1024), 16, 0, 0);
+    });
+  }
+  uint2 braw[FN][4];
+  load_bias16<FN>(p, n_base, half, braw);
+  wait_vmcnt<0>();  // this wave's C copies have landed in its region
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const bool c_bf16 = p.c_type == kBF16, b_bf16 = p.bias_type == kBF16;
+  const float beta = has_c ? p.beta : 0.f;
+  static_for<FM>([&](auto i) {
     static_for<FN>([&](auto j) {
       static_for<4>([&](auto g) {
-        static_for<4>([&](auto q) { bias[j][g][q] = 0.f; });
-        if (p.bias) load4(p.bias, p.bias_type, n_base + 32 * j + 8 * g + 4 * half, bias[j][g]);
+        const int r = 32 * i + row;
+        uint8_t* slot = region + r * kRowB + swz(r, 4 * j + g) * 16 + 8 * half;
+        const uint2 c = has_c ? *(const uint2*)slot : uint2{0u, 0u};
+        *(uint2*)slot = epi_group<kAct, kDBf16>(acc[i][j], g, c, braw[j][g], p.alpha, beta, c_bf16, b_bf16);
       });
     });
-    uint2 c[FM][FN][4];
-    if (p.beta != 0.f) {
-      const uint16_t* C = (const uint16_t*)p.C;
-      static_for<FM>([&](auto i) {
-        static_for<FN>([&](auto j) {
-          static_for<4>([&](auto g) {
-            c[i][j][g] = *(const uint2*)(C + (int64_t)(m_base + 32 * i + row) * p.c_sm + n_base +
-                                         32 * j + 8 * g + 4 * half);
-          });
-        });
-      });
-    }
-    uint16_t* D = (uint16_t*)p.D;
+  });
+  uint8_t* D = p.D + ((int64_t)m_base * p.d_sm + n_base) * 2;
+  static_for<kIters>([&](auto t) {
+    const int r = kRowsPerKiB * t + rr;
+    const i32x4 v = *(const i32x4*)(region + t * 1024 + lane * 16);
+    *(i32x4*)(D + (int64_t)r * p.d_sm * 2 + swz(r, cs) * 16) = v;
+  });
+}
+
+// Full wave tile straight from and to global memory with 8-byte vectors;
+// all C and bias loads are issued before the arithmetic.
+template <int kAct, bool kDBf16, int FM, int FN>
+__device__ __forceinline__ void epilogue_direct(const GemmParams& p, int m_base, int n_base, int lane,
+                                                const f32x16 (&acc)[FM][FN]) {
+  const int row = lane & 31, half = lane >> 5;
+  const bool has_c = p.beta != 0.f;
+  uint2 c[FM][FN][4];
+  if (has_c) {
+    const uint16_t* C = (const uint16_t*)p.C;
     static_for<FM>([&](auto i) {
       static_for<FN>([&](auto j) {
         static_for<4>([&](auto g) {
-          float y[4];
-          static_for<4>([&](auto q) { y[q] = p.alpha * acc[i][j][4 * g + q]; });
-          if (p.beta != 0.f) {
-            const uint32_t w[4] = {c[i][j][g].x & 0xFFFFu, c[i][j][g].x >> 16, c[i][j][g].y & 0xFFFFu,
-                                   c[i][j][g].y >> 16};
-            static_for<4>([&](auto q) {
-              const float cv = p.c_type == kBF16 ? __builtin_bit_cast(float, w[q] << 16)
-                                                 : (float)__builtin_bit_cast(_Float16, (uint16_t)w[q]);
-              y[q] += p.beta * cv;
-            });
-          }
-          static_for<4>([&](auto q) { y[q] = activate(y[q] + bias[j][g][q], p.act); });
-          uint2 u;
-          u.x = (uint32_t)to_bits(y[0], p.d_type) | ((uint32_t)to_bits(y[1], p.d_type) << 16);
-          u.y = (uint32_t)to_bits(y[2], p.d_type) | ((uint32_t)to_bits(y[3], p.d_type) << 16);
-          *(uint2*)(D + (int64_t)(m_base + 32 * i + row) * p.d_sm + n_base + 32 * j + 8 * g + 4 * half) = u;
+          c[i][j][g] = *(const uint2*)(C + (int64_t)(m_base + 32 * i + row) * p.c_sm + n_base + 32 * j +
+                                       8 * g + 4 * half);
         });
       });
     });
+  } else {
+    static_for<FM>([&](auto i) {
+      static_for<FN>([&](auto j) { static_for<4>([&](auto g) { c[i][j][g] = uint2{0u, 0u}; }); });
+    });
+  }
+  uint2 braw[FN][4];
+  load_bias16<FN>(p, n_base, half, braw);
+  const bool c_bf16 = p.c_type == kBF16, b_bf16 = p.bias_type == kBF16;
+  const float beta = has_c ? p.beta : 0.f;
+  uint16_t* D = (uint16_t*)p.D;
+  static_for<FM>([&](auto i) {
+    static_for<FN>([&](auto j) {
+      static_for<4>([&](auto g) {
+        *(uint2*)(D + (int64_t)(m_base + 32 * i + row) * p.d_sm + n_base + 32 * j + 8 * g + 4 * half) =
+            epi_group<kAct, kDBf16>(acc[i][j], g, c[i][j][g], braw[j][g], p.alpha, beta, c_bf16, b_bf16);
+      });
+    });
+  });
+}
+
+template <bool kLds, int kAct, bool kDBf16, int FM, int FN>
+__device__ __forceinline__ void epilogue_fast(const GemmParams& p, int m_base, int n_base, int lane,
+                                              const f32x16 (&acc)[FM][FN], uint8_t* region) {
+  if constexpr (kLds)
+    epilogue_lds<kAct, kDBf16, FM, FN>(p, m_base, n_base, lane, acc, region);
+  else
+    epilogue_direct<kAct, kDBf16, FM, FN>(p, m_base, n_base, lane, acc);
+}
+
+template <bool kLds, int FM, int FN>
+__device__ __forceinline__ void epilogue_switch(const GemmParams& p, int m_base, int n_base, int lane,
+                                                const f32x16 (&acc)[FM][FN], uint8_t* region) {
+  const bool dbf = p.d_type == kBF16;
+  switch (p.act) {
+    case TLA_ACT_RELU:
+      if (dbf) epilogue_fast<kLds, TLA_ACT_RELU, true>(p, m_base, n_base, lane, acc, region);
+      else epilogue_fast<kLds, TLA_ACT_RELU, false>(p, m_base, n_base, lane, acc, region);
+      break;
+    case TLA_ACT_GELU:
+      if (dbf) epilogue_fast<kLds, TLA_ACT_GELU, true>(p, m_base, n_base, lane, acc, region);
+      else epilogue_fast<kLds, TLA_ACT_GELU, false>(p, m_base, n_base, lane, acc, region);
+      break;
+    default:
+      if (dbf) epilogue_fast<kLds, TLA_ACT_NONE, true>(p, m_base, n_base, lane, acc, region);
+      else epilogue_fast<kLds, TLA_ACT_NONE, false>(p, m_base, n_base, lane, acc, region);
+      break;
+  }
+}
+
+// The epilogue of one wavefront's FM x FN grid of 32x32 accumulator tiles,
+// rows m_base + 32i + lane%32, column groups n_base + 32j + 8g + 4(lane/32).
+// `region` is this wave's 32*FM x 64*FN-byte piece of LDS, free for reuse
+// (the caller has synchronised the workgroup after its last LDS read), or
+// null.  A wave tile inside D with 16-bit C (or no C) and bias takes the LDS
+// path when C and D rows allow 16-byte vectors, else the direct path with
+// 8-byte vectors; anything else (edge tiles, fp32 C or bias, strided C or D)
+// goes group by group through the predicated epilogue4.
+template <int FM, int FN>
+__device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, int n_base, int lane,
+                                               const f32x16 (&acc)[FM][FN], uint8_t* region) {
+  const bool full = m_base + 32 * FM <= p.M && n_base + 32 * FN <= p.N;
+  const bool b_ok = !p.bias || ((p.flags & kBiasVec) && p.bias_type != kF32);
+  const bool c16 = p.c_type != kF32;
+  if (full && b_ok && region && (p.flags & kD16) && (p.beta == 0.f || (c16 && (p.flags & kC16)))) {
+    epilogue_switch<true, FM, FN>(p, m_base, n_base, lane, acc, region);
+  } else if (full && b_ok && (p.flags & kDVec) && (p.beta == 0.f || (c16 && (p.flags & kCVec)))) {
+    epilogue_switch<false, FM, FN>(p, m_base, n_base, lane, acc, region);
   } else {
     static_for<FM>([&](auto i) {
       const int m = m_base + 32 * i + mfma32_acc_col(lane, 0);
@@ -524,10 +661,15 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
         if (kt + 1 < KT) tile(kt + 1, std::integral_constant<int, 1>{});
       }
     }
-    wait_vmcnt<0>();  // no copy may land in LDS after the workgroup ends
+    wait_vmcnt<0>();  // no copy may land in LDS after this point
   }
 
-  epilogue_tiles<FM, FN>(p, m0 + wm0, n0 + wn0, lane, acc);
+  // Every wave is past its last LDS read: the stages become the waves'
+  // epilogue regions.
+  constexpr bool kLdsEpi = (NT / 64) * WM * 64 * FN <= kStages * STAGE;
+  __syncthreads();
+  epilogue_tiles<FM, FN>(p, m0 + wm0, n0 + wn0, lane, acc,
+                         kLdsEpi ? smem + wave * WM * 64 * FN : nullptr);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -680,8 +822,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 
   // Epilogue: acc[i][j] holds the D^T piece for rows m0+wm0+32i.. and
   // columns n0+wn0+32j..; value r of lane l sits at (row, col) =
-  // (lane%32, mfma32_acc_row(l, r)) of that 32x32 piece.
-  epilogue_tiles<FM, FN>(p, m0 + wm0, n0 + wn0, lane, acc);
+  // (lane%32, mfma32_acc_row(l, r)) of that 32x32 piece.  No copy is in
+  // flight here; after the barrier the stages are the waves' regions.
+  constexpr bool kLdsEpi = 4 * WM * 64 * FN <= kStages * STAGE;
+  __syncthreads();
+  epilogue_tiles<FM, FN>(p, m0 + wm0, n0 + wn0, lane, acc,
+                         kLdsEpi ? smem + wave * WM * 64 * FN : nullptr);
 }
 
 // ----------------------------------------------------------------- dispatch
@@ -778,6 +924,8 @@ int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const 
   const int ceb = elem_bytes(g.c_type), beb = elem_bytes(g.bias_type);
   if (g.C && g.c_order == TLA_ROW_MAJOR && (g.ldc % 4) == 0 && aligned(g.C, 4 * ceb)) p.flags |= kCVec;
   if (g.d_order == TLA_ROW_MAJOR && (g.ldd % 4) == 0 && aligned(g.D, 8)) p.flags |= kDVec;
+  if (g.C && ceb == 2 && g.c_order == TLA_ROW_MAJOR && (g.ldc % 8) == 0 && aligned(g.C, 16)) p.flags |= kC16;
+  if (g.d_order == TLA_ROW_MAJOR && (g.ldd % 8) == 0 && aligned(g.D, 16)) p.flags |= kD16;
   if (g.bias && aligned(g.bias, 4 * beb)) p.flags |= kBiasVec;
   const bool a_vec = (g.a_order == TLA_ROW_MAJOR) && ((g.lda * eb) % 16 == 0) && aligned(g.A, 16);
   const bool b_vec = (g.b_order == TLA_COL_MAJOR) && ((g.ldb * eb) % 16 == 0) && aligned(g.B, 16);

@@ -131,7 +131,10 @@ int transpose_dispatch(const void* src, int64_t ld_src, void* dst, int64_t ld_ds
                        int64_t N, int eb, hipStream_t s) {
   if (eb == 4 && M % 4 == 0 && N % 4 == 0 && ld_src % 4 == 0 && ld_dst % 4 == 0 && aligned16(src) &&
       aligned16(dst)) {
-    constexpr int TI = 2, TJ = 2;
+    // a 64 x 256 block tile: 1 KiB runs per source row and 256-byte runs per
+    // destination column in each block; measured fastest of the 4x4-micro-tile
+    // shapes on a 16384^2 fp32 copy (taller tiles and multi-tile blocks lose)
+    constexpr int TI = 1, TJ = 4;
     const int64_t tm = (M + 64 * TI - 1) / (64 * TI), tn = (N + 64 * TJ - 1) / (64 * TJ);
     if (tm * tn > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((transpose4_kernel<TI, TJ>), dim3((unsigned)(tm * tn)), dim3(256), 0, s,
