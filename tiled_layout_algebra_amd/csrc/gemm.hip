@@ -523,90 +523,146 @@ __device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, 
 }
 
 // ------------------------------------------------------------- fast kernel
+// 16 bytes per lane from base + voffset + soffset into LDS, landing
+// lane-linearly from the wave-uniform address `lds`: a raw buffer load whose
+// per-lane 32-bit offset and uniform offset stay separate registers, so the
+// loop spends no vector instructions on copy addresses.  Every offset the
+// kernel forms is below 2^31 (checked by the host).
+__device__ __forceinline__ void dma16_buf(const uint8_t* base, uint32_t voffset, uint32_t soffset,
+                                          uint8_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset,
+                                           soffset, 0, 0);
+#endif
+}
+
 // Both operands K-contiguous with 16-byte aligned rows, K a multiple of the
-// slab width.  kStages LDS stages of BM + BN rows x kRowBytes; k-tile kt
-// lives in stage kt % kStages.
+// slab width.  LDS holds kStages A slabs, then kStages B slabs; k-tile kt
+// lives in slot kt % kStages of both.
 //
 // Schedule (one software pipeline over every MFMA k-step of every tile):
-//  * the direct HBM -> LDS copies of tile kt + kStages - 1 are issued one
+//  * the direct global -> LDS copies of tile kt + kStages - 1 are issued one
 //    instruction at a time between the MFMAs of tile kt, so copy issue never
-//    blocks the matrix cores and each copy has kStages - 2 tiles of MFMA work
-//    to land in;
+//    blocks the matrix cores;
 //  * the fragments of step g+1 are read from LDS at the start of step g;
 //  * half-way through the last step of tile kt every wave waits for tile
-//    kt+1 and meets at one barrier, which also frees tile kt-1's stage for
+//    kt+1 and meets at one barrier, which also frees tile kt-1's slot for
 //    the next copy.
-// Past the end of K the copies reload the last k-tile into the free stage,
-// so every tile issues the same number of copies and the wait counts are
-// constants.
+// Past the end of K the copies reload the last k-tile, so every tile issues
+// the same number of copies and the wait counts are constants.
+//
+// Addressing is out of the loop: a copy is a buffer load with a per-lane
+// offset fixed for the whole kernel plus the tile's K offset in a scalar
+// register, and a fragment read is one of a few per-lane base registers
+// plus an immediate (slot and tile row).  The XOR swizzle only sees row bits
+// below 32, so one base per k-step serves every 32-row fragment; grouping
+// the A slots and the B slots keeps every immediate below 64 KiB.
 template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront = 0, int kWM = 2,
           int kWN = 2>
 __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmParams p) {
   using Atom = MfmaAtom<kCode>;
   using Frag = typename Atom::Frag;
+  using Swz = typename Slab<kRowBytes>::Swz;
   constexpr int NT = 64 * kWM * kWN;  // kWM x kWN wavefronts
   constexpr int EB = elem_bytes(kCode);
   constexpr int BK = kRowBytes / EB;
   constexpr int WM = BM / kWM, WN = BN / kWN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int KSTEPS = BK / Atom::kK;
-  static_assert(KSTEPS >= 1 && BK % Atom::kK == 0, "slab narrower than one MFMA step");
-  static_assert(kStages >= 2, "copies need a free stage");
-  constexpr int SLAB_A = BM * kRowBytes, STAGE = (BM + BN) * kRowBytes;
-  static_assert(kStages * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(BK % Atom::kK == 0 && KSTEPS >= 2 && KSTEPS % 2 == 0,
+                "fragment buffers alternate per step");
+  static_assert(kStages >= 2, "copies need a free slot");
+  constexpr int SLAB_A = BM * kRowBytes, SLAB_B = BN * kRowBytes;
+  constexpr int B_BASE = kStages * SLAB_A;
+  static_assert(kStages * (SLAB_A + SLAB_B) <= 160 * 1024, "LDS budget");
+  static_assert(kStages * SLAB_A <= 65536 && kStages * SLAB_B <= 65536, "fragment immediates");
   constexpr int kChunks = Slab<kRowBytes>::kChunks;
+  static_assert((1 << Slab<kRowBytes>::kRowShift) * kChunks <= 32, "swizzle period divides 32 rows");
   constexpr int IA = BM * kChunks / NT, IB = BN * kChunks / NT;
+  static_assert(IA * NT == BM * kChunks && IB * NT == BN * kChunks, "whole copy instructions");
   constexpr int kLoads = IA + IB;                  // copies per thread per tile
-  constexpr int kReads = (FM + FN) * (Atom::kLaneBytes / 16);
+  constexpr int kSub = Atom::kLaneBytes / 16;      // 16-byte reads per fragment
+  constexpr int kReads = (FM + FN) * kSub;
   constexpr int kMfmas = FM * FN;
+  constexpr int kStepBytes = Atom::kK * EB;
   // Copies per full step, the rest go into the first half of the last step.
-  // kFront > 0 puts all copies into the first kFront steps instead (as early
-  // as possible, for shallow pipelines).
+  // kFront > 0 puts all copies into the first kFront steps instead.
   constexpr int kSpread = kFront > 0 && kFront < KSTEPS ? kFront : KSTEPS;
-  constexpr int kPerStep = KSTEPS > 1 ? (kLoads + kSpread - 1) / kSpread : 0;
+  constexpr int kPerStep = (kLoads + kSpread - 1) / kSpread;
   constexpr int kFull = kPerStep * (KSTEPS - 1) < kLoads ? kPerStep * (KSTEPS - 1) : kLoads;
   constexpr int kLast = kLoads - kFull;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * STAGE];
+  constexpr int kWait = (kStages - 2) * kLoads;  // copies allowed in flight past the next tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * (SLAB_A + SLAB_B)];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
   schedule(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int wm0 = (wave % kWM) * WM, wn0 = (wave / kWM) * WN;
-  const int64_t a_rb = p.a_sr * EB, b_rb = p.b_sr * EB;
   const int KT = p.K / BK;
+
+  // Copy q (A for q < IA, else B): slab row r = tid/kChunks + (NT/kChunks)*q',
+  // landing at slab slot wave*64 + NT*q' (lane-linear); the lane fetches the
+  // global chunk the swizzle assigns to that slot, from row r clamped to the
+  // matrix (rows past M or N are never stored).
+  uint32_t off[kLoads];
+  static_for<kLoads>([&](auto q) {
+    constexpr bool kA = q < IA;
+    constexpr int qq = kA ? q : q - IA;
+    const int r = tid / kChunks + (NT / kChunks) * qq;
+    const int64_t row = kA ? min(m0 + r, p.M - 1) : min(n0 + r, p.N - 1);
+    const int64_t rb = (kA ? p.a_sr : p.b_sr) * EB;
+    off[q] = (uint32_t)(row * rb + Swz::chunk(r, tid % kChunks) * 16);
+  });
+  // Fragment bases for each k-step (and each 16-byte half of a 32-byte
+  // fragment): row wm0 + lane%32 of the A slot, wn0 + lane%32 of the B slot.
+  uint32_t fa[KSTEPS][kSub], fb[KSTEPS][kSub];
+  static_for<KSTEPS>([&](auto ks) {
+    static_for<kSub>([&](auto u) {
+      const int c = (ks * kStepBytes + (lane >> 5) * Atom::kLaneBytes) / 16 + u;
+      const int ra = wm0 + (lane & 31), rb = wn0 + (lane & 31);
+      fa[ks][u] = (uint32_t)(ra * kRowBytes + Swz::chunk(ra, c) * 16);
+      fb[ks][u] = (uint32_t)(B_BASE + rb * kRowBytes + Swz::chunk(rb, c) * 16);
+    });
+  });
 
   f32x16 acc[FM][FN];
   static_for<FM>([&](auto i) { static_for<FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
   Frag a[2][FM], b[2][FN];
-  auto read_frags = [&](auto buf, const uint8_t* stage, auto ks) {
-    static_for<FM>([&](auto i) {
-      a[buf][i] = load_frag<kCode, kRowBytes>(stage, wm0 + 32 * i + (lane & 31), ks, lane);
-    });
-    static_for<FN>([&](auto j) {
-      b[buf][j] = load_frag<kCode, kRowBytes>(stage + SLAB_A, wn0 + 32 * j + (lane & 31), ks, lane);
-    });
+  auto lds_frag = [&](const uint32_t (&base)[kSub], int imm) -> Frag {
+    if constexpr (kSub == 1) {
+      return *(const i32x4*)(smem + base[0] + imm);
+    } else {
+      const i32x4 lo = *(const i32x4*)(smem + base[0] + imm);
+      const i32x4 hi = *(const i32x4*)(smem + base[1] + imm);
+      return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  auto read_frags = [&](auto buf, auto slot, auto ks) {
+    static_for<FM>([&](auto i) { a[buf][i] = lds_frag(fa[ks], slot * SLAB_A + i * 32 * kRowBytes); });
+    static_for<FN>([&](auto j) { b[buf][j] = lds_frag(fb[ks], slot * SLAB_B + j * 32 * kRowBytes); });
   };
   auto mma = [&](auto buf, auto idx) {
     Atom::mma(acc[idx / FN][idx % FN], b[buf][idx % FN], a[buf][idx / FN]);
   };
-  // copy q (0 .. kLoads-1) of tile t into its stage; tiles past K reload the last one
-  auto copy = [&](int t, auto q) {
-    uint8_t* st = smem + (t % kStages) * STAGE;
-    const int64_t kb = (int64_t)min(t, KT - 1) * kRowBytes;
+  // copy q of tile t into slot `slot`; tiles past K reload the last one
+  auto copy = [&](int t, auto slot, auto q) {
+    const uint32_t kb = (uint32_t)min(t, KT - 1) * kRowBytes;
     if constexpr (q < IA)
-      dma_one<BM, kRowBytes, NT>(p.A, a_rb, m0, p.M, kb, st, tid, q);
+      dma16_buf(p.A, off[q], kb, smem + slot * SLAB_A + (wave * 64 + NT * q) * 16);
     else
-      dma_one<BN, kRowBytes, NT>(p.B, b_rb, n0, p.N, kb, st + SLAB_A, tid, q - IA);
+      dma16_buf(p.B, off[q], kb, smem + B_BASE + slot * SLAB_B + (wave * 64 + NT * (q - IA)) * 16);
   };
   // MFMAs [lo, hi) of a step with copies [q0, q0 + nq) of tile t spread
   // evenly between them: after MFMA k come copies [k*nq/n, (k+1)*nq/n).
-  auto mfmas_with_copies = [&](auto buf, auto lo, auto hi, int t, auto q0, auto nq) {
+  auto mfmas_with_copies = [&](auto buf, auto lo, auto hi, int t, auto slot, auto q0, auto nq) {
     constexpr int n = hi - lo;
     static_for<n>([&](auto k) {
       mma(buf, std::integral_constant<int, lo + k>{});
       constexpr int c0 = k * nq / n, c1 = (k + 1) * nq / n;
-      static_for<c1 - c0>([&](auto c) { copy(t, std::integral_constant<int, q0 + c0 + c>{}); });
+      static_for<c1 - c0>([&](auto c) { copy(t, slot, std::integral_constant<int, q0 + c0 + c>{}); });
     });
     static_for<n>([&](auto k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -614,30 +670,29 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
       if constexpr (c1 > c0) __builtin_amdgcn_sched_group_barrier(0x020, c1 - c0, 0);
     });
   };
-  constexpr int kWait = (kStages - 2) * kLoads;  // copies allowed in flight past the next tile
-
-  auto tile = [&](int kt, auto parity) {
-    const uint8_t* stage = smem + (kt % kStages) * STAGE;
+  // k-tile kt, which lives in slot S (= kt % kStages)
+  auto tile = [&](int kt, auto S) {
+    using Next = std::integral_constant<int, (S + 1) % kStages>;
+    using Fill = std::integral_constant<int, (S + kStages - 1) % kStages>;
     const int ct = kt + kStages - 1;  // tile whose copies are issued now
     static_for<KSTEPS>([&](auto ks) {
-      constexpr int cur = (parity + ks) & 1;
+      constexpr int cur = ks & 1;
       if constexpr (ks + 1 < KSTEPS) {
-        read_frags(std::integral_constant<int, cur ^ 1>{}, stage, std::integral_constant<int, ks + 1>{});
+        read_frags(std::integral_constant<int, cur ^ 1>{}, S, std::integral_constant<int, ks + 1>{});
         __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
         constexpr int q0 = ks * kPerStep < kFull ? ks * kPerStep : kFull;
         constexpr int q1 = (ks + 1) * kPerStep < kFull ? (ks + 1) * kPerStep : kFull;
         mfmas_with_copies(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
-                          std::integral_constant<int, kMfmas>{}, ct,
+                          std::integral_constant<int, kMfmas>{}, ct, Fill{},
                           std::integral_constant<int, q0>{}, std::integral_constant<int, q1 - q0>{});
       } else {
         mfmas_with_copies(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
-                          std::integral_constant<int, kMfmas / 2>{}, ct,
+                          std::integral_constant<int, kMfmas / 2>{}, ct, Fill{},
                           std::integral_constant<int, kFull>{}, std::integral_constant<int, kLast>{});
         if (kt + 1 < KT) {
           wait_vmcnt<kWait>();  // tile kt+1 landed (this thread's copies)
-          stage_barrier();      // ... everyone's; tile kt-1's stage is free
-          read_frags(std::integral_constant<int, cur ^ 1>{}, smem + ((kt + 1) % kStages) * STAGE,
-                     std::integral_constant<int, 0>{});
+          stage_barrier();      // ... everyone's; tile kt-1's slot is free
+          read_frags(std::integral_constant<int, cur ^ 1>{}, Next{}, std::integral_constant<int, 0>{});
         }
         static_for<kMfmas - kMfmas / 2>([&](auto k) {
           mma(std::integral_constant<int, cur>{}, std::integral_constant<int, kMfmas / 2 + k>{});
@@ -648,25 +703,23 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
 
   if (KT > 0) {
     static_for<kStages - 1>([&](auto t) {
-      static_for<kLoads>([&](auto q) { copy(t, q); });
+      static_for<kLoads>([&](auto q) { copy(t, t, q); });
     });
     wait_vmcnt<kWait>();
     stage_barrier();
-    read_frags(std::integral_constant<int, 0>{}, smem, std::integral_constant<int, 0>{});
-    if constexpr (KSTEPS % 2 == 0) {
-      for (int kt = 0; kt < KT; ++kt) tile(kt, std::integral_constant<int, 0>{});
-    } else {
-      for (int kt = 0; kt < KT; kt += 2) {
-        tile(kt, std::integral_constant<int, 0>{});
-        if (kt + 1 < KT) tile(kt + 1, std::integral_constant<int, 1>{});
-      }
+    read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+               std::integral_constant<int, 0>{});
+    for (int kt = 0; kt < KT; kt += kStages) {
+      static_for<kStages>([&](auto s) {
+        if (kt + s < KT) tile(kt + s, s);
+      });
     }
     wait_vmcnt<0>();  // no copy may land in LDS after this point
   }
 
-  // Every wave is past its last LDS read: the stages become the waves'
+  // Every wave is past its last LDS read: the slots become the waves'
   // epilogue regions.
-  constexpr bool kLdsEpi = (NT / 64) * WM * 64 * FN <= kStages * STAGE;
+  constexpr bool kLdsEpi = (NT / 64) * WM * 64 * FN <= kStages * (SLAB_A + SLAB_B);
   __syncthreads();
   epilogue_tiles<FM, FN>(p, m0 + wm0, n0 + wn0, lane, acc,
                          kLdsEpi ? smem + wave * WM * 64 * FN : nullptr);
@@ -931,7 +984,10 @@ int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const 
   const bool b_vec = (g.b_order == TLA_COL_MAJOR) && ((g.ldb * eb) % 16 == 0) && aligned(g.B, 16);
   p.flags |= (a_vec ? 1 << 8 : 0) | (b_vec ? 1 << 9 : 0);
   const int BK = fast_slab_bytes(g.a_type) / eb;
-  const bool fast = a_vec && b_vec && g.K > 0 && (g.K % BK) == 0;
+  // the fast kernel addresses each operand with 32-bit offsets below 2^31
+  const bool small_ops = (int64_t)g.M * g.lda * eb < (int64_t(1) << 31) &&
+                         (int64_t)g.N * g.ldb * eb < (int64_t(1) << 31);
+  const bool fast = a_vec && b_vec && small_ops && g.K > 0 && (g.K % BK) == 0;
   const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256);
   const bool big = tiles256 >= 128;
   switch (g.a_type) {
