@@ -920,8 +920,9 @@ int launch_two_stage(const GemmParams& p0, hipStream_t stream) {
 // K rows per copy (the direct-to-LDS copy rate per compute unit halves with
 // every halving of the row width), so K must be a multiple of 128 bytes.
 //   16-bit, >= 128 tiles of 256x256: 8 wavefronts (2x4, 128x64 each), two
-//     stages, each tile's copies issued during the first two MFMA steps of
-//     the tile before.
+//     stages, each tile's copies issued during the first MFMA step of the
+//     tile before (measured ~1 % ahead of spreading them over two or all
+//     four steps).
 //   16-bit, smaller: 128x128, 4 wavefronts, three stages.
 //   e4m3: the two-stage kernel (its 32-byte fragments do not fit the
 //     8-wavefront register budget).
@@ -938,7 +939,7 @@ int dispatch_typed(const GemmParams& p, bool fast, bool big, hipStream_t s, bool
     if (v == 0) return launch_two_stage<kCode, 256, 256, 128, true>(p, s);
     if (v == 1) return launch_two_stage<kCode, 128, 128, 128, true>(p, s);
   } else {
-    if (v == 0) return launch_fast<kCode, 256, 256, 128, 2, 2, 2, 4>(p, s);
+    if (v == 0) return launch_fast<kCode, 256, 256, 128, 2, 1, 2, 4>(p, s);
     if (v == 1) return launch_fast<kCode, 128, 128, 128, 3, 1, 2, 2>(p, s);
   }
   return launch_two_stage<kCode, 128, 128, 128, false>(p, s);
