@@ -209,6 +209,59 @@ int tla_thread_map_eval(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I,
                         int32_t contiguous_dim, int64_t rows_valid, int64_t cols_valid,
                         int64_t *out_index, uint8_t *out_valid, void *stream);
 
+/* ------------------------------------------------ layout algebra (host) */
+/*
+ * logical_product of two layouts, in the reading "Advanced CUTLASS
+ * Architecture and Kernel Optimization", "Advanced Layout Operations" gives
+ * it: the result's shape and stride are the concatenations of the inputs'.
+ * out has L's modes followed by M's (n_modes(L) + n_modes(M) <= 8, leaves
+ * <= 16), so as a function of the 1-D index
+ *   out(i) = L(i mod size(L)) + M(i / size(L)).
+ * TLA_ERR_INVALID_ARG for a malformed input or a result past the limits.
+ */
+int tla_logical_product(const tla_layout *L, const tla_layout *M, tla_layout *out);
+
+/*
+ * The flattest layout with L's function: every leaf of extent 1 dropped and
+ * neighbouring leaves merged while stride[k+1] == shape[k] * stride[k].
+ * out is flat (one leaf per mode) when at most 8 leaves remain, else one
+ * mode holding them all; out(i) == L(i) for every i < size(L), and no two
+ * neighbouring leaves of out could merge again.  A layout of size 1 becomes
+ * 1:0.  Host only.
+ */
+int tla_coalesce(const tla_layout *L, tla_layout *out);
+
+/*
+ * A o B in closed form ("Functional Composition": c -> A(B(c))): a layout R
+ * with B's top-level modes such that R(i) == A(B(i)) for every i < size(B),
+ * A taking B's value as a 1-D index.  Every B(i) must lie in
+ * [0, size(A)) (TLA_ERR_INVALID_ARG otherwise, as for tla_layout_eval).
+ * Each leaf s:d of B becomes the run of A's (coalesced) modes that the
+ * indices 0, d, ..., (s-1)d walk: d must be a product of whole leading
+ * extents of A times a divisor of the next one, and s must end on or
+ * inside a mode boundary the same way; the leaves of B must cover disjoint
+ * ranges of A's mixed radix (sorted by stride, d' >= d*s), so that A adds
+ * their contributions without carries.  When these hold the closed form is
+ * exact; otherwise TLA_ERR_UNSUPPORTED (use the pointwise tla_layout_eval).
+ * TLA_ERR_UNSUPPORTED also when the result needs more than 16 leaves.
+ */
+int tla_composition(const tla_layout *A, const tla_layout *B, tla_layout *out);
+
+/*
+ * logical_divide of every mode, nested modes included: mode i of L (size
+ * n_i, any nesting) and tile t_i give two top-level modes of out, the
+ * position inside the tile and the tile index, in the order
+ * (inside_0, index_0, inside_1, index_1, ...) -- 2 * n_modes(L) <= 8.
+ * inside_i (e < t_i) and index_i (q < ceil(n_i / t_i)) stand for the
+ * element at 1-D position e + t_i * q of mode i.  A nested mode is divided
+ * by composing it with (t_i, n_i/t_i):(1, t_i), so t_i must divide n_i and
+ * the composition must have a closed form (TLA_ERR_UNSUPPORTED otherwise);
+ * a one-leaf mode n:d may be divided raggedly into (t_i:d,
+ * ceil(n/t_i):d*t_i), the last tile reaching past the end.  Host only.
+ */
+int tla_logical_divide_modes(const tla_layout *L, const int64_t *tile, int32_t n_tile,
+                             tla_layout *out);
+
 /* ------------------------------------------------------------- misc */
 const char *tla_status_string(int status);
 int tla_version(void);

@@ -276,6 +276,73 @@ def tiled_divide(L: Layout, tile) -> TiledDivided:
     return TiledDivided(L, tile)
 
 
+# ---------------------------------------------------- product and nested divide
+
+def modes_of(L: Layout):
+    """Top-level modes of L as (shape, stride) pairs (an integer shape is one
+    mode)."""
+    if is_int(L.shape):
+        return [(L.shape, L.stride)]
+    return list(zip(L.shape, L.stride))
+
+
+def logical_product(L: Layout, M: Layout) -> Layout:
+    """logical_product in the reading of "Advanced Layout Operations": the
+    shape and the stride of the result are the concatenations of the
+    inputs' (L's modes first, then M's)."""
+    ml, mm = modes_of(L), modes_of(M)
+    return Layout(tuple(s for s, _ in ml + mm), tuple(d for _, d in ml + mm))
+
+
+class DividedModes:
+    """logical_divide of every top-level mode of L, nested modes included.
+
+    Mode i (shape s_i, stride d_i, size n_i) and tile t_i become two modes,
+    the position e < t_i inside the tile and the tile index
+    q < ceil(n_i / t_i), and stand for the element at 1-D position
+    e + t_i * q of mode i, taken through that mode's own colexicographic
+    idx2crd ("Advanced Layout Operations": one mode becomes a tile mode and a
+    mode inside the tile).  The result's modes are ordered
+    (inside_0, index_0, inside_1, index_1, ...).
+
+    A flat mode n:d maps its coordinate linearly, so a ragged last tile
+    keeps the value x*d past the end (as Divided does); for a nested mode
+    the tile must divide the mode's size.
+    """
+
+    def __init__(self, L: Layout, tile):
+        self.modes = modes_of(L)
+        tile = (tile,) if is_int(tile) else tuple(tile)
+        if len(tile) != len(self.modes) or any(t <= 0 for t in tile):
+            raise ValueError("one positive tile extent per mode is required")
+        self.tile = tile
+        self.rest = []
+        for (s, _), t in zip(self.modes, tile):
+            n = size(s)
+            if not is_int(s) and n % t:
+                raise ValueError("a nested mode needs a tile dividing its size")
+            self.rest.append(ceil_div(n, t))
+        self.shape = tuple(x for t, r in zip(tile, self.rest) for x in (t, r))
+
+    def size(self) -> int:
+        return size(self.shape)
+
+    def __call__(self, i: int) -> int:
+        crd = idx2crd(i, self.shape)
+        total = 0
+        for k, ((s, d), t) in enumerate(zip(self.modes, self.tile)):
+            x = crd[2 * k] + t * crd[2 * k + 1]
+            total += x * d if is_int(s) else crd2idx(idx2crd(x, s), s, d)
+        return total
+
+    def table(self):
+        return [self(i) for i in range(self.size())]
+
+
+def divide_modes(L: Layout, tile) -> DividedModes:
+    return DividedModes(L, tile)
+
+
 # ---------------------------------------------------------- local_partition
 
 def thread_coord(thr_layout: Layout, tid: int):

@@ -137,3 +137,44 @@ def test_thread_map_eval_brute_force():
                     for t in range(T):
                         want[t + T * (v + V * it)] = int(tm.valid(t, it, v, rows, cols))
             assert val == want
+
+
+# -------------------------------------------- layout algebra results on device
+
+def test_algebra_results_on_device():
+    """Closed-form composition, nested divide, product and coalesce
+    descriptors evaluated by the device module, against the oracle's
+    pointwise definitions."""
+    sm80 = (((4, 8), (2, 2, 2)), ((32, 1), (16, 8, 128)))
+    # the pages' chain: vectors of 2, arranged in a column-walking matrix
+    # view, over two batched 6x8 row-major matrices
+    mem = tla.make_layout((8, 6, 2), (1, 8, 48))
+    mat = tla.make_layout(((2, 4), 6, 2), ((1, 2), 8, 48))
+    vec = tla.make_layout((2, 48), (1, 2))
+    chain = tla.composition(tla.composition(mem, mat), vec)
+    want = L.Composition(L.Composition(L.Layout((8, 6, 2), (1, 8, 48)),
+                                       L.Layout(((2, 4), 6, 2), ((1, 2), 8, 48))),
+                         L.Layout((2, 48), (1, 2))).table()
+    assert _dev_table(chain) == want
+    d = tla.logical_divide_modes(tla.make_layout(*sm80), (8, 4))
+    assert _dev_table(d) == L.divide_modes(L.Layout(*sm80), (8, 4)).table()
+    p = tla.logical_product(tla.make_layout((4, 8), (8, 1)), tla.make_layout(3, 32))
+    assert _dev_table(p) == L.logical_product(L.Layout((4, 8), (8, 1)), L.Layout(3, 32)).table()
+    c = tla.coalesce(tla.make_layout(((2, 2), 4, 1, 3), ((1, 2), 4, 7, 16)))
+    assert _dev_table(c) == L.Layout(((2, 2), 4, 1, 3), ((1, 2), 4, 7, 16)).table()
+
+
+def test_composed_tiled_view_at_scale():
+    """A 512x512 row-major matrix seen as 16x16 tiles of 32x32, tile row
+    fastest: the closed form from tla_composition, evaluated on the device
+    over all 2^18 entries, equals A(B(i)) computed one entry at a time."""
+    A = tla.make_layout((512, 512), (512, 1))
+    B = tla.make_layout(((32, 32), (16, 16)), ((1, 512), (32, 16384)))
+    R = tla.composition(A, B)
+    got = _dev_table(R)
+    a, b = L.Layout((512, 512), (512, 1)), L.Layout(((32, 32), (16, 16)), ((1, 512), (32, 16384)))
+    rng = random.Random(4)
+    for i in rng.sample(range(len(got)), 4096) + [0, len(got) - 1]:
+        assert got[i] == a(b(i))
+    # and the device's pointwise composition agrees everywhere
+    assert got == _dev_table(A, B)

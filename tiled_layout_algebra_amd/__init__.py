@@ -26,7 +26,8 @@ MAX_MODES, MAX_LEAVES = 8, 16
 EXPORTED = [
     "tla_gemm_epilogue", "tla_gemm_variant", "tla_tiled_transpose", "tla_layout_size",
     "tla_layout_eval", "tla_logical_divide", "tla_tiled_divide", "tla_thread_map",
-    "tla_thread_map_eval", "tla_status_string", "tla_version",
+    "tla_thread_map_eval", "tla_logical_product", "tla_coalesce", "tla_composition",
+    "tla_logical_divide_modes", "tla_status_string", "tla_version",
 ]
 
 
@@ -85,6 +86,10 @@ def lib() -> ctypes.CDLL:
         L.tla_tiled_divide.argtypes = [LP, ctypes.POINTER(I64), I32, LP]
         L.tla_thread_map.argtypes = [I64, I64, I32, I32, I32, I32, LP]
         L.tla_thread_map_eval.argtypes = [I64, I64, I32, I32, I32, I32, I64, I64, P, P, P]
+        L.tla_logical_product.argtypes = [LP, LP, LP]
+        L.tla_coalesce.argtypes = [LP, LP]
+        L.tla_composition.argtypes = [LP, LP, LP]
+        L.tla_logical_divide_modes.argtypes = [LP, ctypes.POINTER(I64), I32, LP]
         L.tla_status_string.argtypes = [ctypes.c_int]
         L.tla_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -234,6 +239,32 @@ def logical_divide(d: LayoutDesc, tile) -> LayoutDesc:
 
 def tiled_divide(d: LayoutDesc, tile) -> LayoutDesc:
     return _divide(lib().tla_tiled_divide, d, tile)
+
+
+def logical_divide_modes(d: LayoutDesc, tile) -> LayoutDesc:
+    """Every mode (nested ones too) split into (inside, index) top-level modes."""
+    return _divide(lib().tla_logical_divide_modes, d, tile)
+
+
+def logical_product(a: LayoutDesc, b: LayoutDesc) -> LayoutDesc:
+    out = LayoutDesc()
+    _check(lib().tla_logical_product(ctypes.byref(a), ctypes.byref(b), ctypes.byref(out)),
+           "tla_logical_product")
+    return out
+
+
+def coalesce(d: LayoutDesc) -> LayoutDesc:
+    out = LayoutDesc()
+    _check(lib().tla_coalesce(ctypes.byref(d), ctypes.byref(out)), "tla_coalesce")
+    return out
+
+
+def composition(a: LayoutDesc, b: LayoutDesc) -> LayoutDesc:
+    """Closed-form a o b; TlaError with status UNSUPPORTED when it has none."""
+    out = LayoutDesc()
+    _check(lib().tla_composition(ctypes.byref(a), ctypes.byref(b), ctypes.byref(out)),
+           "tla_composition")
+    return out
 
 
 def thread_map(R, C, T, V, I, contiguous_dim=1) -> LayoutDesc:

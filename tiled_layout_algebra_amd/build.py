@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtla.so")
-SOURCES = ["api.cpp", "gemm.hip", "transpose.hip", "layout_eval.hip"]
+SOURCES = ["api.cpp", "algebra.cpp", "gemm.hip", "transpose.hip", "layout_eval.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
