@@ -209,6 +209,33 @@ int tla_thread_map_eval(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I,
                         int32_t contiguous_dim, int64_t rows_valid, int64_t cols_valid,
                         int64_t *out_index, uint8_t *out_valid, void *stream);
 
+/*
+ * The two optional parameters of the same walk-through (0 / -1 = off; the
+ * plain functions above are these with both off):
+ *  - threads_per_row G (section 2.2, which lets a parameter override the
+ *    default thread distribution): G threads share one strided position
+ *    instead of Q/V; a thread then makes Ic = (Q/V)/G passes along the
+ *    contiguous dimension (innermost) per strided step:
+ *      column group = (t mod G) + G*(it mod Ic),
+ *      strided      = t div G + (it div Ic)*S,   S = T/G,
+ *    requiring G | Q/V, G | T, Ic | I and P == S*(I/Ic);
+ *  - swizzle_shift s >= 0 (section 5.3, a map that exchanges bits of the
+ *    thread-to-address mapping to spread bank conflicts): the column group
+ *    is XORed with (strided >> s) mod (Q/V), Q/V a power of two -- a
+ *    permutation of the groups at every strided position.
+ * tla_thread_map_ex returns the unswizzled map's TV layout
+ *   ((G, T/G), (V, Ic, I/Ic)) : ((V, Q), (1, G*V, S*Q))
+ * (the two-leaf value mode of tla_thread_map when Ic == 1); a swizzled map
+ * is not a shape/stride layout and is only evaluated on the device.
+ * TLA_ERR_INVALID_ARG when a requirement fails.
+ */
+int tla_thread_map_ex(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I,
+                      int32_t contiguous_dim, int32_t threads_per_row, tla_layout *out);
+int tla_thread_map_eval_ex(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I,
+                           int32_t contiguous_dim, int32_t threads_per_row, int32_t swizzle_shift,
+                           int64_t rows_valid, int64_t cols_valid, int64_t *out_index,
+                           uint8_t *out_valid, void *stream);
+
 /* ------------------------------------------------ layout algebra (host) */
 /*
  * logical_product of two layouts, in the reading "Advanced CUTLASS

@@ -393,9 +393,23 @@ class StripMinedThreadMap:
     column-major variant of section 3.4 with the roles of rows and columns
     swapped: rows are split into groups of V and the iterations step along
     columns.
+
+    Two options of the same walk-through, off by default:
+
+    * ``threads_per_row`` (section 2.2: the base map takes a parameter that
+      overrides the default thread distribution).  Reading: G threads share
+      one row instead of C/V; each thread then makes Ic = (C/V)/G passes
+      along the row (innermost) per row step, so iteration it is the pass
+      it mod Ic of row step it div Ic:
+        column group = t mod G + G*(it mod Ic),  row = t div G + (it div Ic)*S,
+      with S = T/G the row stride and R == S*(I/Ic).
+    * ``swizzle_shift`` (section 5.3: a map that exchanges bits of the
+      thread-to-address mapping to spread bank conflicts).  Reading: the
+      column group is XORed with (row >> shift) mod (C/V), C/V a power of
+      two -- every row's groups are permuted among themselves.
     """
 
-    def __init__(self, R, C, T, V, I, contiguous_dim=1):
+    def __init__(self, R, C, T, V, I, contiguous_dim=1, threads_per_row=0, swizzle_shift=-1):
         if min(R, C, T, V, I) <= 0:
             raise ValueError("all extents must be positive")
         if R * C != T * V * I:
@@ -405,19 +419,29 @@ class StripMinedThreadMap:
         P, Q = (R, C) if contiguous_dim == 1 else (C, R)  # P strided, Q contiguous
         if Q % V:
             raise ValueError("vector width must divide the contiguous extent")
-        self.G = Q // V
-        if T % self.G or P % I:
+        self.groups = Q // V
+        self.G = threads_per_row if threads_per_row > 0 else self.groups
+        if self.groups % self.G:
+            raise ValueError("threads per row must divide the column groups")
+        self.Ic = self.groups // self.G
+        if T % self.G or I % self.Ic:
             raise ValueError("threads do not tile the strided extent")
-        self.S = P // I
-        if self.S != T // self.G:
-            raise ValueError("row stride R/I differs from the thread rows T/G")
+        self.S = T // self.G
+        if P != self.S * (I // self.Ic):
+            raise ValueError("row stride times row steps differs from the strided extent")
+        if swizzle_shift >= 0 and self.groups & (self.groups - 1):
+            raise ValueError("a swizzle needs a power-of-two number of column groups")
+        self.shift = swizzle_shift
 
     def coord(self, t, it, v):
         """(row, col) visited by thread t, iteration it, vector lane v."""
         if not (0 <= t < self.T and 0 <= it < self.I and 0 <= v < self.V):
             raise IndexError("(t, it, v) out of range")
-        strided = t // self.G + it * self.S
-        contiguous = (t % self.G) * self.V + v
+        strided = t // self.G + (it // self.Ic) * self.S
+        group = t % self.G + self.G * (it % self.Ic)
+        if self.shift >= 0:
+            group ^= (strided >> self.shift) % self.groups
+        contiguous = group * self.V + v
         return (strided, contiguous) if self.contig == 1 else (contiguous, strided)
 
     def index(self, t, it, v):
@@ -443,10 +467,17 @@ class StripMinedThreadMap:
         """The same map as a (thread, value) layout: thread modes (G, T/G),
         value modes (V, I), into the tile index.  Reading (the page states
         the map as formulas only): strides ((V, Q), (1, S*Q)) with Q the
-        contiguous extent."""
+        contiguous extent; with several passes per row the iteration mode
+        splits into (Ic, I/Ic) with strides (G*V, S*Q).  A swizzled map is
+        not a shape/stride layout."""
+        if self.shift >= 0:
+            raise ValueError("a swizzled map has no shape/stride form")
         Q = self.C if self.contig == 1 else self.R
-        return Layout(((self.G, self.T // self.G), (self.V, self.I)),
-                      ((self.V, Q), (1, self.S * Q)))
+        if self.Ic == 1:
+            return Layout(((self.G, self.T // self.G), (self.V, self.I)),
+                          ((self.V, Q), (1, self.S * Q)))
+        return Layout(((self.G, self.T // self.G), (self.V, self.Ic, self.I // self.Ic)),
+                      ((self.V, Q), (1, self.G * self.V, self.S * Q)))
 
     def table(self):
         """out[t + T*(v + V*it)] = index(t, it, v): the TV layout's 1-D table

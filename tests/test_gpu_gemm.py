@@ -236,3 +236,25 @@ def test_repeatable():
     case = _small(M=512, N=512, K=512, act=W.ACT_NONE)
     inp = W.gemm_inputs(case)
     assert np.array_equal(G.run_gemm(case, inp), G.run_gemm(case, inp))
+
+
+# ----------------------------------------------- pitched operands at scale
+
+def test_fast_path_pitched_at_scale():
+    """4096 x 4096 x 1024 bf16 with every pitch past its extent (NaN in the
+    operand padding, a sentinel in D's): the 256x256 fast kernel and the
+    whole-row LDS epilogue read and write through the pitch."""
+    case = _small(M=4096, N=4096, K=1024, act=W.ACT_RELU, seed=21)
+    case.lda, case.ldb, case.ldc, case.ldd = 1024 + 64, 1024 + 8, 4096 + 8, 4096 + 24
+    assert G.variant(case) == "gemm_fast_256x256"
+    _check_sampled(case, W.gemm_inputs(case), seed=3)
+
+
+def test_general_path_pitched_at_scale():
+    """3000 x 2500 x 700 fp16, B row-major (N contiguous), odd
+    pitches everywhere: the register-staged general path at scale."""
+    case = _small(M=3000, N=2500, K=700, a_type=W.F16, b_type=W.F16, d_type=W.F16,
+                  b_order=W.ROW, act=W.ACT_GELU, seed=22)
+    case.lda, case.ldb, case.ldc, case.ldd = 700 + 3, 2500 + 5, 2500 + 1, 2500 + 7
+    assert G.variant(case) == "gemm_general_128x128"
+    _check_sampled(case, W.gemm_inputs(case), seed=4)

@@ -178,3 +178,36 @@ def test_composed_tiled_view_at_scale():
         assert got[i] == a(b(i))
     # and the device's pointwise composition agrees everywhere
     assert got == _dev_table(A, B)
+
+
+# -------------------------------------------------- thread-map variants on device
+
+def _map_eval_ex(R, C, T, V, I, contig, G, shift, rows, cols):
+    n = T * V * I
+    idx = torch.full((n,), -1, dtype=torch.int64, device="cuda")
+    val = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+    tla.thread_map_eval_ex(R, C, T, V, I, contig, G, shift, rows, cols, idx, val)
+    torch.cuda.synchronize()
+    return idx.cpu().tolist(), val.cpu().tolist()
+
+
+VARIANTS = [  # (R, C, T, V, I, contig, threads_per_row, swizzle_shift)
+    (64, 64, 128, 4, 8, 1, 16, -1), (64, 64, 128, 4, 8, 1, 8, -1), (64, 64, 128, 4, 8, 1, 4, -1),
+    (64, 64, 128, 4, 8, 1, 16, 0), (64, 64, 128, 4, 8, 1, 8, 2), (64, 64, 128, 4, 8, 0, 8, 1),
+    (256, 8, 256, 1, 8, 1, 0, 1),            # the GEMM slab's swizzled copy
+    (128, 64, 256, 8, 4, 1, 4, 1), (32, 128, 64, 8, 8, 1, 4, 0), (16, 16, 16, 2, 8, 1, 2, 1),
+]
+
+
+@pytest.mark.parametrize("R,C,T,V,I,contig,G,shift", VARIANTS)
+def test_thread_map_variants_on_device(R, C, T, V, I, contig, G, shift):
+    tm = L.StripMinedThreadMap(R, C, T, V, I, contig, threads_per_row=G, swizzle_shift=shift)
+    for rows, cols in [(R, C), (R - 1, C - 3), (R // 2 + 1, 1)]:
+        idx, val = _map_eval_ex(R, C, T, V, I, contig, G, shift, rows, cols)
+        assert idx == tm.table()
+        want = [0] * (T * V * I)
+        for it in range(I):
+            for v in range(V):
+                for t in range(T):
+                    want[t + T * (v + V * it)] = int(tm.valid(t, it, v, rows, cols))
+        assert val == want

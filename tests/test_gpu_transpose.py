@@ -92,3 +92,16 @@ def test_transpose_full_size_fp32_bits():
     torch.cuda.synchronize()
     assert torch.equal(d2, s)
     assert torch.equal(d3, d)
+
+
+@pytest.mark.parametrize("ps,pd,eb", [(4, 12, 4), (3, 5, 4), (8, 16, 2)])
+def test_transpose_pitched_at_scale(ps, pd, eb):
+    """8192 x 4096 with row pitches past the extents (the pitch taken from the
+    layout, walk-through section 6.3): 16-byte aligned pitches take the fast
+    path, odd ones the general one; every element and every padding element
+    of the destination is compared."""
+    case = W.TransposeCase(name="t", M=8192, N=4096, ld_src=4096 + ps, ld_dst=8192 + pd,
+                           elem_bytes=eb, seed=77 + ps)
+    src = _src(case)
+    got, dst0 = _run(case, src)
+    assert np.array_equal(got, _oracle(case, src, dst0))

@@ -27,7 +27,8 @@ EXPORTED = [
     "tla_gemm_epilogue", "tla_gemm_variant", "tla_tiled_transpose", "tla_layout_size",
     "tla_layout_eval", "tla_logical_divide", "tla_tiled_divide", "tla_thread_map",
     "tla_thread_map_eval", "tla_logical_product", "tla_coalesce", "tla_composition",
-    "tla_logical_divide_modes", "tla_status_string", "tla_version",
+    "tla_logical_divide_modes", "tla_thread_map_ex", "tla_thread_map_eval_ex",
+    "tla_status_string", "tla_version",
 ]
 
 
@@ -90,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.tla_coalesce.argtypes = [LP, LP]
         L.tla_composition.argtypes = [LP, LP, LP]
         L.tla_logical_divide_modes.argtypes = [LP, ctypes.POINTER(I64), I32, LP]
+        L.tla_thread_map_ex.argtypes = [I64, I64, I32, I32, I32, I32, I32, LP]
+        L.tla_thread_map_eval_ex.argtypes = [I64, I64, I32, I32, I32, I32, I32, I32, I64, I64,
+                                             P, P, P]
         L.tla_status_string.argtypes = [ctypes.c_int]
         L.tla_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -272,6 +276,22 @@ def thread_map(R, C, T, V, I, contiguous_dim=1) -> LayoutDesc:
     _check(lib().tla_thread_map(R, C, T, V, I, contiguous_dim, ctypes.byref(out)),
            "tla_thread_map")
     return out
+
+
+def thread_map_ex(R, C, T, V, I, contiguous_dim=1, threads_per_row=0) -> LayoutDesc:
+    out = LayoutDesc()
+    _check(lib().tla_thread_map_ex(R, C, T, V, I, contiguous_dim, threads_per_row,
+                                   ctypes.byref(out)), "tla_thread_map_ex")
+    return out
+
+
+def thread_map_eval_ex(R, C, T, V, I, contiguous_dim, threads_per_row, swizzle_shift, rows_valid,
+                       cols_valid, out_index, out_valid=None, stream=None):
+    _check(lib().tla_thread_map_eval_ex(R, C, T, V, I, contiguous_dim, threads_per_row,
+                                        swizzle_shift, rows_valid, cols_valid,
+                                        _dev(out_index, "out_index"), _dev(out_valid, "out_valid"),
+                                        _stream(stream, out_index)),
+           "tla_thread_map_eval_ex")
 
 
 def thread_map_eval(R, C, T, V, I, contiguous_dim, rows_valid, cols_valid, out_index,

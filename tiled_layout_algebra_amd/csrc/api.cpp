@@ -150,11 +150,13 @@ int divide(const tla_layout* L, const int64_t* tile, int32_t n_tile, tla_layout*
   return TLA_OK;
 }
 
-int check_thread_map(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I, int32_t contig) {
+int check_thread_map(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I, int32_t contig,
+                     int32_t threads_per_row = 0, int32_t swizzle_shift = -1) {
   if (R < 1 || C < 1 || T < 1 || V < 1 || I < 1) return TLA_ERR_INVALID_ARG;
   if (contig != 0 && contig != 1) return TLA_ERR_INVALID_ARG;
+  if (threads_per_row < 0 || swizzle_shift < -1) return TLA_ERR_INVALID_ARG;
   if (R > (1 << 20) || C > (1 << 20) || R * C > (int64_t(1) << 28)) return TLA_ERR_INVALID_ARG;
-  const StripMinedMap map((int)R, (int)C, T, V, I, contig);
+  const StripMinedMap map((int)R, (int)C, T, V, I, contig, threads_per_row, swizzle_shift);
   return map.well_formed() ? TLA_OK : TLA_ERR_INVALID_ARG;
 }
 
@@ -234,32 +236,57 @@ int tla_tiled_divide(const tla_layout* L, const int64_t* tile, int32_t n_tile, t
   return divide(L, tile, n_tile, out, true);
 }
 
-int tla_thread_map(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I, int32_t contiguous_dim,
-                   tla_layout* out) {
+int tla_thread_map_ex(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I,
+                      int32_t contiguous_dim, int32_t threads_per_row, tla_layout* out) {
   if (!out) return TLA_ERR_INVALID_ARG;
-  const int rc = check_thread_map(R, C, T, V, I, contiguous_dim);
+  const int rc = check_thread_map(R, C, T, V, I, contiguous_dim, threads_per_row);
   if (rc) return rc;
-  const StripMinedMap map((int)R, (int)C, T, V, I, contiguous_dim);
-  const Layout<4, int> tv = map.tv_layout();
+  const StripMinedMap map((int)R, (int)C, T, V, I, contiguous_dim, threads_per_row);
   memset(out, 0, sizeof(*out));
   out->n_modes = 2;
   out->leaves[0] = 2;
-  out->leaves[1] = 2;
-  for (int i = 0; i < 4; ++i) {
-    out->shape[i] = tv.shape[i];
-    out->stride[i] = tv.stride[i];
+  if (map.Ic == 1) {
+    const Layout<4, int> tv = map.tv_layout();
+    out->leaves[1] = 2;
+    for (int i = 0; i < 4; ++i) {
+      out->shape[i] = tv.shape[i];
+      out->stride[i] = tv.stride[i];
+    }
+  } else {
+    // ((G, T/G), (V, Ic, I/Ic)) : ((V, Q), (1, G*V, S*Q))
+    out->leaves[1] = 3;
+    const int64_t shape[5] = {map.G, map.T / map.G, map.V, map.Ic, map.I / map.Ic};
+    const int64_t stride[5] = {map.V, map.Q, 1, (int64_t)map.G * map.V, (int64_t)map.S * map.Q};
+    for (int i = 0; i < 5; ++i) {
+      out->shape[i] = shape[i];
+      out->stride[i] = stride[i];
+    }
   }
   return TLA_OK;
+}
+
+int tla_thread_map(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I, int32_t contiguous_dim,
+                   tla_layout* out) {
+  return tla_thread_map_ex(R, C, T, V, I, contiguous_dim, 0, out);
+}
+
+int tla_thread_map_eval_ex(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I,
+                           int32_t contiguous_dim, int32_t threads_per_row, int32_t swizzle_shift,
+                           int64_t rows_valid, int64_t cols_valid, int64_t* out_index,
+                           uint8_t* out_valid, void* stream) {
+  const int rc = check_thread_map(R, C, T, V, I, contiguous_dim, threads_per_row, swizzle_shift);
+  if (rc) return rc;
+  if (!out_index || rows_valid < 0 || cols_valid < 0) return TLA_ERR_INVALID_ARG;
+  return thread_map_eval_dispatch((int)R, (int)C, T, V, I, contiguous_dim, threads_per_row,
+                                  swizzle_shift, rows_valid, cols_valid, out_index, out_valid,
+                                  (hipStream_t)stream);
 }
 
 int tla_thread_map_eval(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I,
                         int32_t contiguous_dim, int64_t rows_valid, int64_t cols_valid,
                         int64_t* out_index, uint8_t* out_valid, void* stream) {
-  const int rc = check_thread_map(R, C, T, V, I, contiguous_dim);
-  if (rc) return rc;
-  if (!out_index || rows_valid < 0 || cols_valid < 0) return TLA_ERR_INVALID_ARG;
-  return thread_map_eval_dispatch((int)R, (int)C, T, V, I, contiguous_dim, rows_valid, cols_valid,
-                                  out_index, out_valid, (hipStream_t)stream);
+  return tla_thread_map_eval_ex(R, C, T, V, I, contiguous_dim, 0, -1, rows_valid, cols_valid,
+                                out_index, out_valid, stream);
 }
 
 const char* tla_status_string(int status) {

@@ -39,8 +39,8 @@ struct FlatLayout {
 int layout_eval_dispatch(const FlatLayout& outer, const FlatLayout& inner, bool has_inner,
                          int64_t* out, int64_t n, hipStream_t stream);
 
-int thread_map_eval_dispatch(int R, int C, int T, int V, int I, int contig, int64_t rows_valid,
-                             int64_t cols_valid, int64_t* out_index, uint8_t* out_valid,
-                             hipStream_t stream);
+int thread_map_eval_dispatch(int R, int C, int T, int V, int I, int contig, int threads_per_row,
+                             int swizzle_shift, int64_t rows_valid, int64_t cols_valid,
+                             int64_t* out_index, uint8_t* out_valid, hipStream_t stream);
 
 }  // namespace tla

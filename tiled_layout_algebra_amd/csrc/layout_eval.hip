@@ -79,10 +79,10 @@ int layout_eval_dispatch(const FlatLayout& outer, const FlatLayout& inner, bool 
   return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
 }
 
-int thread_map_eval_dispatch(int R, int C, int T, int V, int I, int contig, int64_t rows_valid,
-                             int64_t cols_valid, int64_t* out_index, uint8_t* out_valid,
-                             hipStream_t stream) {
-  const StripMinedMap map(R, C, T, V, I, contig);
+int thread_map_eval_dispatch(int R, int C, int T, int V, int I, int contig, int threads_per_row,
+                             int swizzle_shift, int64_t rows_valid, int64_t cols_valid,
+                             int64_t* out_index, uint8_t* out_valid, hipStream_t stream) {
+  const StripMinedMap map(R, C, T, V, I, contig, threads_per_row, swizzle_shift);
   const int64_t total = (int64_t)T * V * I;
   if (total == 0) return TLA_OK;
   const int64_t blocks = (total + 255) / 256;
