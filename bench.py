@@ -13,6 +13,7 @@ one write of the matrix) is reported beside it, each with its roofline.
 `cpu_baseline` times the oracle on a bounded row sample of the same GEMM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --sweep [--steps K] [--warmup W]   # GEMM variant x shape table
 """
 import argparse
 import json
@@ -41,7 +42,66 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="append a plain 1 GiB device-to-device copy to every step (a kernel "
                          "of known traffic, for scaling HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the JSON line: time every compiled GEMM variant on a "
+                         "set of shapes and print a table with each kernel's occupancy")
     return ap.parse_args()
+
+
+SWEEP_SHAPES = [(1024, 1024, 1024), (2048, 2048, 2048), (4096, 4096, 4096), (8192, 8192, 2048)]
+
+
+def sweep(steps, warmup):
+    """Tile-configuration sweep: every variant x shape x operand type, plain
+    D = A.B (bf16 D), inputs U[-1,1] seeded; occupancy from the runtime."""
+    import torch
+    import tiled_layout_algebra_amd as tla
+    import workloads as W
+    from tests.gpu_util import to_dev
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    peaks = {W.BF16: PEAK_BF16_TFLOPS, W.E4M3: 2 * PEAK_BF16_TFLOPS}
+    lines = ["| type | variant | tile | threads | LDS KiB | regs/lane | WGs/CU | waves/SIMD "
+             "| M×N×K | tiles | µs | TFLOP/s | % peak | auto |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for a_type, tname in ((W.BF16, "bf16"), (W.E4M3, "e4m3")):
+        infos = [tla.gemm_variant_info(v, a_type) for v in range(tla.GEMM_VARIANTS)]
+        for M, N, K in SWEEP_SHAPES:
+            case = W.GemmCase(name="sweep", M=M, N=N, K=K, a_type=a_type, b_type=a_type,
+                              d_type=W.BF16, seed=7)
+            inp = W.gemm_inputs(case)
+            dA, dB = to_dev(inp["A"]), to_dev(inp["B"])
+            dD = torch.empty(M * N, dtype=torch.int16, device="cuda")
+            call = (M, N, K, dA, a_type, case.a_order, case.lda, dB, a_type, case.b_order,
+                    case.ldb, dD, W.BF16, case.d_order, case.ldd)
+            auto = tla.gemm_variant(*call)
+            for v, info in enumerate(infos):
+                def run():
+                    tla.gemm_epilogue(*call, stream=stream.cuda_stream, variant=v)
+                for _ in range(warmup):
+                    run()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(steps):
+                    run()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / steps
+                tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+                bm = info["block_m"]
+                tiles = -(-M // bm) * -(-N // bm)
+                waves = info["blocks_per_cu"] * info["threads"] / 64 / 4
+                lines.append("| %s | %s | %d×%d | %d | %d | %d | %d | %g | %d×%d×%d | %d | %.1f "
+                             "| %.0f | %.1f | %s |" % (
+                                 tname, info["name"], bm, bm, info["threads"],
+                                 info["lds_bytes"] // 1024, info["vgprs"], info["blocks_per_cu"],
+                                 waves, M, N, K, tiles, us, tf, 100 * tf / peaks[a_type],
+                                 "←" if info["name"] == auto else ""))
+                print(lines[-1], file=sys.stderr, flush=True)
+            del dA, dB, dD
+    print("\n".join(lines), flush=True)
 
 
 CSRC = os.path.join(ROOT, "tiled_layout_algebra_amd", "csrc")
@@ -106,6 +166,9 @@ def main():
         print("bench.py measures one GPU: this library has no multi-GPU path; run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        sweep(max(args.steps, 1), args.warmup)
+        return
 
     import torch
     import tiled_layout_algebra_amd as tla

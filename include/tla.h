@@ -118,6 +118,38 @@ int tla_gemm_epilogue(const tla_gemm_args *args, void *stream);
  * (written NUL-terminated into buf, at most cap bytes).  Host only. */
 int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
 
+/*
+ * Tile-configuration dispatch ("CUTLASS / CuTe 主线", the kernel-composition
+ * and profiling lesson; the ThreadblockShape trade-off between reuse and
+ * occupancy).  The library compiles TLA_GEMM_VARIANTS kernels:
+ *   0 "gemm_fast_256x256"    256x256 tiles (16-bit: 8 wavefronts;
+ *                            e4m3: 4), direct global->LDS copies
+ *   1 "gemm_fast_128x128"    128x128 tiles, 4 wavefronts, direct copies
+ *   2 "gemm_general_128x128" 128x128 tiles, register-staged predicated
+ *                            loads: any order, pitch, alignment, ragged K
+ * tla_gemm_epilogue picks one from the problem: in the fast layout,
+ * variant 0 for 16-bit operands with at least 128 tiles of 256x256 and 1
+ * otherwise (e4m3 always 1, measured faster); variant 2 outside it;
+ * tla_gemm_run_variant runs the one asked for, with the same semantics and
+ * tolerance, or returns TLA_ERR_UNSUPPORTED when a fast variant is asked
+ * for a problem without the fast layout (both operands K-contiguous,
+ * 16-byte aligned rows, K a multiple of 128 bytes, each operand < 2 GiB).
+ * Variant ids outside [0, TLA_GEMM_VARIANTS) are TLA_ERR_INVALID_ARG.
+ */
+#define TLA_GEMM_VARIANTS 3
+int tla_gemm_run_variant(const tla_gemm_args *args, int32_t variant, void *stream);
+
+/* A variant's compiled kernel for operand type a_type, as the HIP runtime
+ * reports it on the current device: threads per workgroup, static LDS bytes,
+ * vector registers per lane and the number of workgroups that can be
+ * resident on one compute unit.  Needs a device (TLA_ERR_HIP without). */
+typedef struct {
+  char name[32];
+  int32_t block_m, block_n, threads;
+  int32_t lds_bytes, vgprs, blocks_per_cu;
+} tla_gemm_kernel_info;
+int tla_gemm_variant_info(int32_t variant, int32_t a_type, tla_gemm_kernel_info *out);
+
 /* --------------------------------------------------------- transpose */
 /*
  * dst(m, n) = src(m, n) bit for bit, from a row-major source to a

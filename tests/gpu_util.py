@@ -29,7 +29,7 @@ def to_host(t: torch.Tensor, like: np.dtype) -> np.ndarray:
     return t.cpu().numpy().view(like)
 
 
-def run_gemm(case: W.GemmCase, inp: dict, sentinel=None, pad_front=0, d_is_c=False):
+def run_gemm(case: W.GemmCase, inp: dict, sentinel=None, pad_front=0, d_is_c=False, variant=None):
     """One tla_gemm_epilogue call; returns the D storage array (host)."""
     dA = to_dev(inp["A"], pad_front) if inp["A"] is not None else None
     dB = to_dev(inp["B"], pad_front) if inp["B"] is not None else None
@@ -43,7 +43,7 @@ def run_gemm(case: W.GemmCase, inp: dict, sentinel=None, pad_front=0, d_is_c=Fal
                       dB, case.b_type, case.b_order, case.ldb, dD, case.d_type, case.d_order,
                       case.ldd, C=dC, c_type=case.c_type, c_order=case.c_order, ldc=case.ldc,
                       bias=dbias, bias_type=case.bias_type, alpha=case.alpha, beta=case.beta,
-                      scale_a=case.scale_a, scale_b=case.scale_b, act=case.act)
+                      scale_a=case.scale_a, scale_b=case.scale_b, act=case.act, variant=variant)
     torch.cuda.synchronize()
     return to_host(dD, W.STORAGE[case.d_type])
 

@@ -160,7 +160,7 @@ def test_e4m3_general_path_ragged_k():
 
 def test_e4m3_8192_full_size_sampled():
     case = W.GEMM_E4M3_8192
-    assert G.variant(case) == "gemm_fast_256x256"
+    assert G.variant(case) == "gemm_fast_128x128"
     _check_sampled(case, W.gemm_inputs(case))
 
 
@@ -258,3 +258,50 @@ def test_general_path_pitched_at_scale():
     case.lda, case.ldb, case.ldc, case.ldd = 700 + 3, 2500 + 5, 2500 + 1, 2500 + 7
     assert G.variant(case) == "gemm_general_128x128"
     _check_sampled(case, W.gemm_inputs(case), seed=4)
+
+
+# ------------------------------------------------- tile-configuration dispatch
+
+@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("a_type,d_type", [(W.BF16, W.BF16), (W.F16, W.F16), (W.E4M3, W.BF16)])
+def test_forced_variants_bit_exact(variant, a_type, d_type):
+    """Every compiled variant, forced through tla_gemm_run_variant on the
+    same integer-valued problem (exact in fp32), gives D bit for bit; the
+    M/N extents are ragged for all three tilings."""
+    M, N, K = 300, 520, 384
+    case = W.GemmCase(name="forced", M=M, N=N, K=K, a_type=a_type, b_type=a_type,
+                      d_type=d_type, alpha=1.5, beta=0.5, act=W.ACT_RELU, has_c=True,
+                      has_bias=True, seed=91, dist_a="int3", dist_b="int3", dist_c="int3",
+                      dist_bias="eighths")
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT[d_type], variant=variant)
+    assert G.padding_untouched(case, D, SENT[d_type])
+    want = W.encode(G.oracle_ref(case, inp), d_type).reshape(M, N)
+    assert np.array_equal(W.d_logical(case, D), want)
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_forced_variants_random_inputs(variant):
+    case = _small(M=640, N=768, K=512, act=W.ACT_GELU, seed=92)
+    _check_full(case, W.gemm_inputs(case), variant=variant)
+
+
+def test_forced_fast_variant_refuses_general_layout():
+    import tiled_layout_algebra_amd as tla
+    case = _small(b_order=W.ROW)  # B N-contiguous: no fast layout
+    for variant in (0, 1):
+        with pytest.raises(tla.TlaError) as e:
+            G.run_gemm(case, W.gemm_inputs(case), sentinel=SENT[case.d_type], variant=variant)
+        assert e.value.status == tla.ERR_UNSUPPORTED
+
+
+def test_variant_info_reports_the_compiled_kernels():
+    import tiled_layout_algebra_amd as tla
+    for a_type in (W.BF16, W.F16, W.E4M3):
+        infos = [tla.gemm_variant_info(v, a_type) for v in range(tla.GEMM_VARIANTS)]
+        assert [i["name"] for i in infos] == ["gemm_fast_256x256", "gemm_fast_128x128",
+                                              "gemm_general_128x128"]
+        for i in infos:
+            assert i["threads"] in (256, 512) and i["lds_bytes"] > 0 and i["blocks_per_cu"] >= 1
+            assert i["lds_bytes"] * i["blocks_per_cu"] <= 160 * 1024
+        assert infos[0]["block_m"] == 256 and infos[2]["block_n"] == 128

@@ -24,7 +24,8 @@ ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 MAX_MODES, MAX_LEAVES = 8, 16
 
 EXPORTED = [
-    "tla_gemm_epilogue", "tla_gemm_variant", "tla_tiled_transpose", "tla_layout_size",
+    "tla_gemm_epilogue", "tla_gemm_variant", "tla_gemm_run_variant", "tla_gemm_variant_info",
+    "tla_tiled_transpose", "tla_layout_size",
     "tla_layout_eval", "tla_logical_divide", "tla_tiled_divide", "tla_thread_map",
     "tla_thread_map_eval", "tla_logical_product", "tla_coalesce", "tla_composition",
     "tla_logical_divide_modes", "tla_thread_map_ex", "tla_thread_map_eval_ex",
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
         LP = ctypes.POINTER(LayoutDesc)
         L.tla_gemm_epilogue.argtypes = [ctypes.POINTER(GemmArgs), P]
         L.tla_gemm_variant.argtypes = [ctypes.POINTER(GemmArgs), ctypes.c_char_p, I32]
+        L.tla_gemm_run_variant.argtypes = [ctypes.POINTER(GemmArgs), I32, P]
+        L.tla_gemm_variant_info.argtypes = [I32, I32, ctypes.POINTER(GemmKernelInfo)]
         L.tla_tiled_transpose.argtypes = [P, I64, P, I64, I64, I64, I32, P]
         L.tla_layout_size.argtypes = [LP, ctypes.POINTER(I64)]
         L.tla_layout_eval.argtypes = [LP, LP, P, I64, P]
@@ -150,13 +153,39 @@ def _gemm_args(M, N, K, A, a_type, a_order, lda, B, b_type, b_order, ldb, D, d_t
 def gemm_epilogue(M, N, K, A, a_type, a_order, lda, B, b_type, b_order, ldb, D, d_type,
                   d_order, ldd, C=None, c_type=None, c_order=ROW_MAJOR, ldc=0, bias=None,
                   bias_type=None, alpha=1.0, beta=0.0, scale_a=1.0, scale_b=1.0,
-                  act=ACT_NONE, stream=None):
-    """D = act(alpha*scale_a*scale_b*A.B + beta*C + bias) (tla_gemm_epilogue)."""
+                  act=ACT_NONE, stream=None, variant=None):
+    """D = act(alpha*scale_a*scale_b*A.B + beta*C + bias) (tla_gemm_epilogue);
+    with `variant` (0 .. GEMM_VARIANTS-1) that kernel variant is forced
+    (tla_gemm_run_variant)."""
     args = _gemm_args(M, N, K, A, a_type, a_order, lda, B, b_type, b_order, ldb, D, d_type,
                       d_order, ldd, C, c_type, c_order, ldc, bias, bias_type, alpha, beta,
                       scale_a, scale_b, act)
-    _check(lib().tla_gemm_epilogue(ctypes.byref(args), _stream(stream, A, B, D)),
-           "tla_gemm_epilogue")
+    if variant is None:
+        _check(lib().tla_gemm_epilogue(ctypes.byref(args), _stream(stream, A, B, D)),
+               "tla_gemm_epilogue")
+    else:
+        _check(lib().tla_gemm_run_variant(ctypes.byref(args), variant, _stream(stream, A, B, D)),
+               "tla_gemm_run_variant")
+
+
+GEMM_VARIANTS = 3
+
+
+class GemmKernelInfo(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("block_m", ctypes.c_int32),
+                ("block_n", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("vgprs", ctypes.c_int32),
+                ("blocks_per_cu", ctypes.c_int32)]
+
+
+def gemm_variant_info(variant: int, a_type: int) -> dict:
+    """Compiled-kernel facts of a variant on the current device (needs a GPU)."""
+    out = GemmKernelInfo()
+    _check(lib().tla_gemm_variant_info(variant, a_type, ctypes.byref(out)),
+           "tla_gemm_variant_info")
+    return dict(name=out.name.decode(), block_m=out.block_m, block_n=out.block_n,
+                threads=out.threads, lds_bytes=out.lds_bytes, vgprs=out.vgprs,
+                blocks_per_cu=out.blocks_per_cu)
 
 
 def gemm_epilogue_args(args: GemmArgs, stream) -> int:

@@ -172,6 +172,30 @@ int tla_gemm_epilogue(const tla_gemm_args* args, void* stream) {
   return gemm_dispatch(p, (hipStream_t)stream, false, nullptr);
 }
 
+int tla_gemm_run_variant(const tla_gemm_args* args, int32_t variant, void* stream) {
+  if (variant < 0 || variant >= kGemmVariants) return TLA_ERR_INVALID_ARG;
+  GemmProblem p{};
+  const int rc = validate_gemm(args, &p);
+  if (rc < 0) return rc;
+  if (rc == 1) return TLA_OK;
+  return gemm_dispatch(p, (hipStream_t)stream, false, nullptr, variant);
+}
+
+int tla_gemm_variant_info(int32_t variant, int32_t a_type, tla_gemm_kernel_info* out) {
+  if (!out || variant < 0 || variant >= kGemmVariants) return TLA_ERR_INVALID_ARG;
+  GemmKernelInfo k{};
+  const int rc = gemm_variant_info(a_type, variant, &k);
+  if (rc) return rc;
+  memset(out, 0, sizeof(*out));
+  strncpy(out->name, k.name, sizeof(out->name) - 1);
+  out->block_m = out->block_n = k.tile;
+  out->threads = k.threads;
+  out->lds_bytes = k.lds_bytes;
+  out->vgprs = k.vgprs;
+  out->blocks_per_cu = k.blocks_per_cu;
+  return TLA_OK;
+}
+
 int tla_gemm_variant(const tla_gemm_args* args, char* buf, int32_t cap) {
   if (!buf || cap < 1) return TLA_ERR_INVALID_ARG;
   GemmProblem p{};

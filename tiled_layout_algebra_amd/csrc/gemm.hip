@@ -928,12 +928,20 @@ int launch_two_stage(const GemmParams& p0, hipStream_t stream) {
 //     8-wavefront register budget).
 int fast_slab_bytes(int) { return 128; }
 
+const char* const kVariantNames[kGemmVariants] = {"gemm_fast_256x256", "gemm_fast_128x128",
+                                                  "gemm_general_128x128"};
+const int kVariantTile[kGemmVariants] = {256, 128, 128};
+
 template <int kCode>
 int dispatch_typed(const GemmParams& p, bool fast, bool big, hipStream_t s, bool dry,
-                   const char** name) {
-  static const char* names[3] = {"gemm_fast_256x256", "gemm_fast_128x128", "gemm_general_128x128"};
-  const int v = fast ? (big ? 0 : 1) : 2;
-  if (name) *name = names[v];
+                   const char** name, int forced) {
+  // e4m3: the 128x128 kernel (two workgroups per compute unit) measured
+  // ahead of 256x256 at every size of the variant sweep (8192^3: 644 vs
+  // 725 us), so it is the automatic choice whenever the fast layout holds.
+  const bool use_big = big && kCode != kE4M3;
+  const int v = forced >= 0 ? forced : (fast ? (use_big ? 0 : 1) : 2);
+  if (v < 2 && !fast) return TLA_ERR_UNSUPPORTED;  // a fast variant needs the fast layout
+  if (name) *name = kVariantNames[v];
   if (dry) return TLA_OK;
   if constexpr (kCode == kE4M3) {
     if (v == 0) return launch_two_stage<kCode, 256, 256, 128, true>(p, s);
@@ -945,9 +953,51 @@ int dispatch_typed(const GemmParams& p, bool fast, bool big, hipStream_t s, bool
   return launch_two_stage<kCode, 128, 128, 128, false>(p, s);
 }
 
+// The kernel each variant launches for operand type kCode.
+template <int kCode>
+const void* variant_kernel(int v, int* threads) {
+  *threads = kThreads;
+  if constexpr (kCode == kE4M3) {
+    if (v == 0) return (const void*)gemm_kernel<kCode, 256, 256, 128, 2, true>;
+    if (v == 1) return (const void*)gemm_kernel<kCode, 128, 128, 128, 2, true>;
+  } else {
+    if (v == 0) {
+      *threads = 512;
+      return (const void*)gemm_fast_kernel<kCode, 256, 256, 128, 2, 1, 2, 4>;
+    }
+    if (v == 1) return (const void*)gemm_fast_kernel<kCode, 128, 128, 128, 3, 1, 2, 2>;
+  }
+  return (const void*)gemm_kernel<kCode, 128, 128, 128, 2, false>;
+}
+
 }  // namespace
 
-int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const char** name) {
+int gemm_variant_info(int a_type, int variant, GemmKernelInfo* out) {
+  if (variant < 0 || variant >= kGemmVariants) return TLA_ERR_INVALID_ARG;
+  int threads = 0;
+  const void* k = nullptr;
+  switch (a_type) {
+    case TLA_BF16: k = variant_kernel<kBF16>(variant, &threads); break;
+    case TLA_F16: k = variant_kernel<kF16>(variant, &threads); break;
+    case TLA_E4M3: k = variant_kernel<kE4M3>(variant, &threads); break;
+    default: return TLA_ERR_UNSUPPORTED;
+  }
+  hipFuncAttributes attr{};
+  if (hipFuncGetAttributes(&attr, k) != hipSuccess) return TLA_ERR_HIP;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, threads, 0) != hipSuccess)
+    return TLA_ERR_HIP;
+  out->name = kVariantNames[variant];
+  out->tile = kVariantTile[variant];
+  out->threads = threads;
+  out->lds_bytes = (int)attr.sharedSizeBytes;
+  out->vgprs = attr.numRegs;
+  out->blocks_per_cu = blocks;
+  return TLA_OK;
+}
+
+int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const char** name,
+                  int forced) {
   if (g.M > 0x7FFFFFFF || g.N > 0x7FFFFFFF || g.K > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
   const int eb = elem_bytes(g.a_type);
   GemmParams p{};
@@ -992,9 +1042,9 @@ int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const 
   const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256);
   const bool big = tiles256 >= 128;
   switch (g.a_type) {
-    case TLA_BF16: return dispatch_typed<kBF16>(p, fast, big, stream, dry_run, name);
-    case TLA_F16: return dispatch_typed<kF16>(p, fast, big, stream, dry_run, name);
-    case TLA_E4M3: return dispatch_typed<kE4M3>(p, fast, big, stream, dry_run, name);
+    case TLA_BF16: return dispatch_typed<kBF16>(p, fast, big, stream, dry_run, name, forced);
+    case TLA_F16: return dispatch_typed<kF16>(p, fast, big, stream, dry_run, name, forced);
+    case TLA_E4M3: return dispatch_typed<kE4M3>(p, fast, big, stream, dry_run, name, forced);
     default: return TLA_ERR_UNSUPPORTED;
   }
 }

@@ -25,7 +25,17 @@ struct GemmProblem {
 
 // Picks the kernel variant; launches it unless `dry_run`.  `name` receives
 // the variant's name (may be NULL).
-int gemm_dispatch(const GemmProblem& p, hipStream_t stream, bool dry_run, const char** name);
+// GEMM kernel variants: 0 fast 256x256, 1 fast 128x128, 2 general 128x128.
+constexpr int kGemmVariants = 3;
+struct GemmKernelInfo {
+  const char* name;
+  int tile, threads, lds_bytes, vgprs, blocks_per_cu;
+};
+// forced = -1 picks the variant from the problem; a forced fast variant on a
+// problem without the fast layout returns TLA_ERR_UNSUPPORTED.
+int gemm_dispatch(const GemmProblem& p, hipStream_t stream, bool dry_run, const char** name,
+                  int forced = -1);
+int gemm_variant_info(int a_type, int variant, GemmKernelInfo* out);
 
 int transpose_dispatch(const void* src, int64_t ld_src, void* dst, int64_t ld_dst, int64_t M,
                        int64_t N, int elem_bytes, hipStream_t stream);
