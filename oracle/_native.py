@@ -41,6 +41,20 @@ class GemmArgs(ctypes.Structure):
     ]
 
 
+class ConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int64), ("H", ctypes.c_int64), ("W", ctypes.c_int64),
+        ("C", ctypes.c_int64), ("K", ctypes.c_int64), ("R", ctypes.c_int64),
+        ("S", ctypes.c_int64),
+        ("u", ctypes.c_int32), ("v", ctypes.c_int32), ("ph", ctypes.c_int32),
+        ("pw", ctypes.c_int32), ("dh", ctypes.c_int32), ("dw", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("Cres", ctypes.c_void_p),
+        ("type", ctypes.c_int32),
+        ("bias", ctypes.c_void_p), ("bias_type", ctypes.c_int32), ("act", ctypes.c_int32),
+        ("alpha", ctypes.c_double), ("beta", ctypes.c_double),
+    ]
+
+
 def lib() -> ctypes.CDLL:
     """Load the oracle library, building it first if it is missing or stale."""
     global _lib
@@ -57,6 +71,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_gemm_points.restype = I32
         L.oracle_transpose.argtypes = [P, I64, P, I64, I64, I64, I32]
         L.oracle_transpose.restype = I32
+        L.oracle_conv2d.argtypes = [ctypes.POINTER(ConvArgs), P, I32]
+        L.oracle_conv2d.restype = I32
+        L.oracle_conv2d_points.argtypes = [ctypes.POINTER(ConvArgs), P, P, I64, P, I32]
+        L.oracle_conv2d_points.restype = I32
         L.oracle_version.restype = I32
         _lib = L
     return _lib

@@ -311,4 +311,120 @@ int oracle_transpose(const void *src, int64_t ld_src, void *dst, int64_t ld_dst,
   return 0;
 }
 
+/* ----------------------------------------------------------- convolution */
+
+/* Forward convolution (cross-correlation) as the implicit GEMM of the
+ * PitchLinearStripminedThreadMap walk-through (lpnh.cn/news/2469163),
+ * section 5.2: one GEMM dimension is the output pixel, the other the
+ * filter position times the channel.  Reading (the page gives no formula):
+ * x is N x H x W x C (NHWC), w is K x R x S x C (KRSC), the output N x P x Q x K
+ * (NPQK) with P = (H + 2 ph - dh (R-1) - 1) / u + 1 (Q likewise), and
+ *   s[n,p,q,k] = sum over r < R, s < S, c < C of
+ *                x[n, p u - ph + r dh, q v - pw + s dw, c] * w[k, r, s, c],
+ * x taken as 0 outside the image.  The GEMM epilogue follows at GEMM
+ * position (m = (n P + p) Q + q, k): alpha, beta * Cres[n,p,q,k], bias[k],
+ * activation. */
+typedef struct {
+  int64_t N, H, W, C, K, R, S;
+  int32_t u, v, ph, pw, dh, dw;
+  const void *x; const void *w; const void *Cres; int32_t type;
+  const void *bias; int32_t bias_type; int32_t act;
+  double alpha, beta;
+} oracle_conv_args;
+
+static int64_t conv_out(int64_t in, int64_t f, int32_t stride, int32_t pad, int32_t dil) {
+  const int64_t span = in + 2 * (int64_t)pad - (int64_t)dil * (f - 1) - 1;
+  return span < 0 ? 0 : span / stride + 1;
+}
+
+typedef struct {
+  const oracle_conv_args *a;
+  const double *xd, *wd;
+  oracle_gemm_args g;          /* the epilogue's view: M = NPQ, N = K */
+  int64_t P, Q;
+  const int64_t *ms, *ks;      /* points mode when non-NULL */
+  double *out;
+  int64_t i0, i1;              /* output rows (full) or points */
+} conv_job;
+
+static double conv_sum(const conv_job *j, int64_t m, int64_t k) {
+  const oracle_conv_args *a = j->a;
+  const int64_t q = m % j->Q, p = (m / j->Q) % j->P, n = m / (j->Q * j->P);
+  double s = 0.0;
+  for (int64_t r = 0; r < a->R; ++r) {
+    const int64_t h = p * a->u - a->ph + r * a->dh;
+    if (h < 0 || h >= a->H) continue;
+    for (int64_t t = 0; t < a->S; ++t) {
+      const int64_t w = q * a->v - a->pw + t * a->dw;
+      if (w < 0 || w >= a->W) continue;
+      const double *xr = j->xd + ((n * a->H + h) * a->W + w) * a->C;
+      const double *wr = j->wd + ((k * a->R + r) * a->S + t) * a->C;
+      for (int64_t c = 0; c < a->C; ++c) s += xr[c] * wr[c];
+    }
+  }
+  return s;
+}
+
+static void *conv_run(void *p) {
+  conv_job *j = (conv_job *)p;
+  if (j->ms) {
+    for (int64_t i = j->i0; i < j->i1; ++i)
+      j->out[i] = epilogue(&j->g, conv_sum(j, j->ms[i], j->ks[i]), j->ms[i], j->ks[i]);
+  } else {
+    for (int64_t m = j->i0; m < j->i1; ++m)
+      for (int64_t k = 0; k < j->a->K; ++k)
+        j->out[m * j->a->K + k] = epilogue(&j->g, conv_sum(j, m, k), m, k);
+  }
+  return NULL;
+}
+
+static int conv_common(const oracle_conv_args *a, const int64_t *ms, const int64_t *ks,
+                       int64_t npts, double *out, int nthreads) {
+  if (!a || !out || a->N < 0 || a->H < 1 || a->W < 1 || a->C < 1 || a->K < 1 || a->R < 1 ||
+      a->S < 1 || a->u < 1 || a->v < 1 || a->dh < 1 || a->dw < 1 || a->ph < 0 || a->pw < 0 ||
+      !elem_bytes(a->type) || !a->x || !a->w)
+    return -1;
+  const int64_t P = conv_out(a->H, a->R, a->u, a->ph, a->dh);
+  const int64_t Q = conv_out(a->W, a->S, a->v, a->pw, a->dw);
+  const int64_t nx = a->N * a->H * a->W * a->C, nw = a->K * a->R * a->S * a->C;
+  double *xd = (double *)malloc(sizeof(double) * (size_t)(nx > 0 ? nx : 1));
+  double *wd = (double *)malloc(sizeof(double) * (size_t)nw);
+  if (!xd || !wd) { free(xd); free(wd); return -2; }
+  for (int64_t i = 0; i < nx; ++i) xd[i] = decode_at(a->type, a->x, i);
+  for (int64_t i = 0; i < nw; ++i) wd[i] = decode_at(a->type, a->w, i);
+  oracle_gemm_args g;
+  memset(&g, 0, sizeof(g));
+  g.M = a->N * P * Q; g.N = a->K; g.K = a->R * a->S * a->C;
+  g.C = a->Cres; g.c_type = a->type; g.c_order = OR_ROW; g.ldc = a->K;
+  g.bias = a->bias; g.bias_type = a->bias_type; g.act = a->act;
+  g.alpha = a->alpha; g.beta = a->beta; g.scale_a = g.scale_b = 1.0;
+  const int64_t total = ms ? npts : g.M;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  conv_job jobs[256];
+  for (int t = 0; t < nthreads; ++t) {
+    conv_job *j = &jobs[t];
+    j->a = a; j->xd = xd; j->wd = wd; j->g = g; j->P = P; j->Q = Q;
+    j->ms = ms; j->ks = ks; j->out = out;
+    j->i0 = total * t / nthreads; j->i1 = total * (t + 1) / nthreads;
+    pthread_create(&th[t], NULL, conv_run, j);
+  }
+  for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+  free(xd); free(wd);
+  return 0;
+}
+
+/* ref is N*P*Q x K, row-major. */
+int oracle_conv2d(const oracle_conv_args *a, double *ref, int nthreads) {
+  return conv_common(a, NULL, NULL, 0, ref, nthreads);
+}
+
+/* out[i] = the output at GEMM position (ms[i], ks[i]). */
+int oracle_conv2d_points(const oracle_conv_args *a, const int64_t *ms, const int64_t *ks,
+                         int64_t n, double *out, int nthreads) {
+  if (!ms || !ks || n < 0) return -1;
+  return conv_common(a, ms, ks, n, out, nthreads);
+}
+
 int oracle_version(void) { return 1; }
