@@ -101,6 +101,38 @@ def sweep(steps, warmup):
                                  "←" if info["name"] == auto else ""))
                 print(lines[-1], file=sys.stderr, flush=True)
             del dA, dB, dD
+    # implicit-GEMM convolution (register-staged general kernel, 128x128)
+    lines += ["", "| convolution | N×H×W×C → K, R×S, stride, pad | GEMM M×N×K | µs | TFLOP/s "
+              "| % peak |", "|---|---|---|---|---|---|"]
+    for case in (W.CONV_F16_56,
+                 W.ConvCase(name="conv_f16_n32_28x28x256_k256_3x3", N=32, H=28, W=28, C=256,
+                            K=256, R=3, S=3, pad=(1, 1), dtype=W.F16, act=W.ACT_RELU,
+                            has_bias=True, seed=6)):
+        inp = W.conv_inputs(case)
+        P, Q = case.out_hw()
+        x, w, b = to_dev(inp["x"]), to_dev(inp["w"]), to_dev(inp["bias"])
+        y = torch.empty(case.N * P * Q * case.K, dtype=torch.int16, device="cuda")
+
+        def run():
+            tla.conv2d_fprop(x, w, y, case.N, case.H, case.W, case.C, case.K, case.R, case.S,
+                             case.dtype, case.stride, case.pad, case.dil, bias=b,
+                             bias_type=case.dtype, act=case.act, stream=stream.cuda_stream)
+        for _ in range(warmup):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        M, Kg = case.N * P * Q, case.R * case.S * case.C
+        tf = 2.0 * M * case.K * Kg / (us * 1e-6) / 1e12
+        lines.append("| %s | %d×%d×%d×%d → %d, %d×%d, %s, %s | %d×%d×%d | %.1f | %.0f | %.1f |" % (
+            case.name, case.N, case.H, case.W, case.C, case.K, case.R, case.S, case.stride,
+            case.pad, M, case.K, Kg, us, tf, 100 * tf / PEAK_BF16_TFLOPS))
+        print(lines[-1], file=sys.stderr, flush=True)
     print("\n".join(lines), flush=True)
 
 

@@ -163,6 +163,39 @@ int tla_gemm_variant_info(int32_t variant, int32_t a_type, tla_gemm_kernel_info 
 int tla_tiled_transpose(const void *src, int64_t ld_src, void *dst, int64_t ld_dst,
                         int64_t M, int64_t N, int32_t elem_bytes, void *stream);
 
+/* ------------------------------------------------------ convolution */
+/*
+ * Forward convolution as an implicit GEMM (PitchLinearStripminedThreadMap
+ * walk-through, section 5.2: one GEMM dimension is the output pixel, the
+ * other the filter position times the channel).  Cross-correlation:
+ *   y[n,p,q,k] = act(alpha * sum_{r,s,c} x[n, p*u - ph + r*dh, q*v - pw + s*dw, c]
+ *                                     * w[k, r, s, c]
+ *                    + beta * C[n,p,q,k] + bias[k])
+ * with x taken as 0 outside the image, accumulated in fp32 and rounded to
+ * nearest even.  x is N x H x W x C (NHWC), w is K x R x S x C (KRSC), y and
+ * C are N x P x Q x K (NPQK), all dense and of one type (f16 or bf16); bias
+ * (length K, f16/bf16/f32) may be NULL; C may be NULL when beta == 0 and may
+ * alias y.  P = (H + 2 ph - dh (R-1) - 1) / u + 1 and Q likewise (floor).
+ * The GEMM has M = N*P*Q, N = K, K = R*S*C; each of them must stay below
+ * 2^31.  N == 0, P < 1 or Q < 1 is a no-op.  Strides and dilations must be
+ * >= 1, paddings >= 0, extents >= 1 (TLA_ERR_INVALID_ARG otherwise).
+ */
+typedef struct {
+  int64_t N, H, W, C, K, R, S;
+  int32_t stride_h, stride_w, pad_h, pad_w, dil_h, dil_w;
+  const void *x;
+  const void *w;
+  const void *C_res;
+  void *y;
+  int32_t type;
+  const void *bias;
+  int32_t bias_type;
+  int32_t act;
+  float alpha, beta;
+} tla_conv2d_args;
+
+int tla_conv2d_fprop(const tla_conv2d_args *args, void *stream);
+
 /* ---------------------------------------------------------- layouts */
 /*
  * A shape/stride layout with at most one level of nesting: n_modes

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "tla.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(tla_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(tla_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -214,3 +214,24 @@ def test_run_variant_argument_errors():
     nn = _args(b_order=tla.ROW_MAJOR, ldb=64)
     for v in (0, 1):
         assert tla.lib().tla_gemm_run_variant(ctypes.byref(nn), v, None) == tla.ERR_UNSUPPORTED
+
+
+def _conv(**kw):
+    base = dict(N=1, H=8, W=8, C=16, K=16, R=3, S=3, stride_h=1, stride_w=1, pad_h=1, pad_w=1,
+                dil_h=1, dil_w=1, x=FAKE, w=FAKE, C_res=None, y=FAKE, type=tla.F16, bias=None,
+                bias_type=tla.F16, act=tla.ACT_NONE, alpha=1.0, beta=0.0)
+    base.update(kw)
+    return tla.ConvArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), tla.ERR_INVALID_ARG), (dict(C=0), tla.ERR_INVALID_ARG),
+    (dict(stride_h=0), tla.ERR_INVALID_ARG), (dict(dil_w=0), tla.ERR_INVALID_ARG),
+    (dict(pad_h=-1), tla.ERR_INVALID_ARG), (dict(act=9), tla.ERR_INVALID_ARG),
+    (dict(type=tla.E4M3), tla.ERR_UNSUPPORTED), (dict(x=None), tla.ERR_INVALID_ARG),
+    (dict(beta=0.5), tla.ERR_INVALID_ARG),                       # beta != 0 without C
+    (dict(N=0), tla.OK), (dict(H=2, R=5, pad_h=0), tla.OK),     # empty output: no-op
+])
+def test_conv_argument_errors(kw, status):
+    a = _conv(**kw)
+    assert tla.lib().tla_conv2d_fprop(ctypes.byref(a), None) == status

@@ -1,0 +1,88 @@
+"""Implicit-GEMM convolution parity: tla_conv2d_fprop through the C ABI
+against the direct-convolution oracle on the same seeded inputs.
+
+* integer-valued inputs: every partial sum is exact in fp32, so y must be
+  the oracle's exact result rounded to y's type, bit for bit -- over stride,
+  padding and dilation, channel counts that do and do not fill a 16-byte
+  vector, 1x1 and 5x5 filters, ragged output-channel and pixel counts;
+* random inputs with GELU within the tolerance, C aliasing y;
+* the measured layer (32 x 56 x 56 x 64, 3x3) compared in full.
+Tolerance: |y - ref| <= tol*(1 + |ref|), tol 1e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import tiled_layout_algebra_amd as tla
+import workloads as W
+from oracle import conv as oc
+from oracle import gemm as og
+from tests.gpu_util import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(case, inp):
+    return oc.conv2d(inp["x"], inp["w"], case.N, case.H, case.W, case.C, case.K, case.R,
+                     case.S, case.stride, case.pad, case.dil, case.dtype, Cres=inp["C"],
+                     bias=inp["bias"], bias_type=case.dtype, alpha=case.alpha, beta=case.beta,
+                     act=case.act)
+
+
+def _run(case, inp, alias=False):
+    P, Q = case.out_hw()
+    x, w = to_dev(inp["x"]), to_dev(inp["w"])
+    c = to_dev(inp["C"]) if inp["C"] is not None else None
+    b = to_dev(inp["bias"]) if inp["bias"] is not None else None
+    y = c if alias else torch.full((case.N * P * Q * case.K,), 0x5A5A, dtype=torch.int16,
+                                  device="cuda")
+    tla.conv2d_fprop(x, w, y, case.N, case.H, case.W, case.C, case.K, case.R, case.S,
+                     case.dtype, case.stride, case.pad, case.dil, C_res=c, bias=b,
+                     bias_type=case.dtype, alpha=case.alpha, beta=case.beta, act=case.act)
+    torch.cuda.synchronize()
+    return to_host(y, np.dtype(np.uint16)).reshape(case.N * P * Q, case.K)
+
+
+GEOMETRIES = [  # N, H, W, C, K, R, S, stride, pad, dil
+    (2, 9, 11, 16, 24, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 10, 7, 3, 5, 3, 2, (2, 1), (1, 0), (1, 2)),
+    (3, 8, 8, 8, 130, 1, 1, (1, 1), (0, 0), (1, 1)),
+    (1, 17, 13, 24, 40, 5, 5, (2, 2), (2, 2), (1, 1)),
+    (2, 12, 12, 32, 64, 3, 3, (1, 1), (2, 2), (2, 2)),
+    (1, 6, 20, 40, 7, 2, 4, (3, 2), (0, 1), (1, 1)),
+]
+
+
+@pytest.mark.parametrize("dtype", [W.F16, W.BF16])
+@pytest.mark.parametrize("geom", GEOMETRIES)
+def test_integer_inputs_bit_exact(geom, dtype):
+    N, H, Wd, C, K, R, S, st, pd, dl = geom
+    case = W.ConvCase(name="exact", N=N, H=H, W=Wd, C=C, K=K, R=R, S=S, stride=st, pad=pd,
+                      dil=dl, dtype=dtype, alpha=1.5, beta=0.5, act=W.ACT_RELU, has_c=True,
+                      has_bias=True, seed=N * 1000 + H * 10 + C, dist="int3", dist_bias="eighths")
+    inp = W.conv_inputs(case)
+    got = _run(case, inp)
+    want = W.encode(_oracle(case, inp), dtype).reshape(got.shape)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "%s: %d mismatches, first at %s" % (geom, len(bad), bad[0])
+
+
+def _tolerance(case, got, ref):
+    ok, worst = og.within_tolerance(og.decode(case.dtype, got), ref, case.tol)
+    assert ok, "worst |y-ref|/(1+|ref|) = %g" % worst
+
+
+def test_random_inputs_gelu_and_c_aliasing_y():
+    case = W.ConvCase(name="rand", N=2, H=15, W=14, C=48, K=72, R=3, S=3, stride=(1, 2),
+                      pad=(1, 1), dtype=W.BF16, alpha=0.75, beta=1.0, act=W.ACT_GELU,
+                      has_c=True, has_bias=True, seed=31)
+    inp = W.conv_inputs(case)
+    ref = _oracle(case, inp)
+    _tolerance(case, _run(case, inp), ref)
+    _tolerance(case, _run(case, inp, alias=True), ref)
+
+
+def test_measured_layer_full():
+    case = W.CONV_F16_56
+    inp = W.conv_inputs(case)
+    _tolerance(case, _run(case, inp), _oracle(case, inp))

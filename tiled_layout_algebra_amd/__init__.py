@@ -25,6 +25,7 @@ MAX_MODES, MAX_LEAVES = 8, 16
 
 EXPORTED = [
     "tla_gemm_epilogue", "tla_gemm_variant", "tla_gemm_run_variant", "tla_gemm_variant_info",
+    "tla_conv2d_fprop",
     "tla_tiled_transpose", "tla_layout_size",
     "tla_layout_eval", "tla_logical_divide", "tla_tiled_divide", "tla_thread_map",
     "tla_thread_map_eval", "tla_logical_product", "tla_coalesce", "tla_composition",
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
         L.tla_gemm_epilogue.argtypes = [ctypes.POINTER(GemmArgs), P]
         L.tla_gemm_variant.argtypes = [ctypes.POINTER(GemmArgs), ctypes.c_char_p, I32]
         L.tla_gemm_run_variant.argtypes = [ctypes.POINTER(GemmArgs), I32, P]
+        L.tla_conv2d_fprop.argtypes = [ctypes.POINTER(ConvArgs), P]
         L.tla_gemm_variant_info.argtypes = [I32, I32, ctypes.POINTER(GemmKernelInfo)]
         L.tla_tiled_transpose.argtypes = [P, I64, P, I64, I64, I64, I32, P]
         L.tla_layout_size.argtypes = [LP, ctypes.POINTER(I64)]
@@ -166,6 +168,33 @@ def gemm_epilogue(M, N, K, A, a_type, a_order, lda, B, b_type, b_order, ldb, D, 
     else:
         _check(lib().tla_gemm_run_variant(ctypes.byref(args), variant, _stream(stream, A, B, D)),
                "tla_gemm_run_variant")
+
+
+class ConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int64), ("H", ctypes.c_int64), ("W", ctypes.c_int64),
+        ("C", ctypes.c_int64), ("K", ctypes.c_int64), ("R", ctypes.c_int64),
+        ("S", ctypes.c_int64),
+        ("stride_h", ctypes.c_int32), ("stride_w", ctypes.c_int32),
+        ("pad_h", ctypes.c_int32), ("pad_w", ctypes.c_int32),
+        ("dil_h", ctypes.c_int32), ("dil_w", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("C_res", ctypes.c_void_p),
+        ("y", ctypes.c_void_p), ("type", ctypes.c_int32),
+        ("bias", ctypes.c_void_p), ("bias_type", ctypes.c_int32), ("act", ctypes.c_int32),
+        ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+    ]
+
+
+def conv2d_fprop(x, w, y, N, H, W, C, K, R, S, dtype, stride=(1, 1), pad=(0, 0), dil=(1, 1),
+                 C_res=None, bias=None, bias_type=None, alpha=1.0, beta=0.0, act=ACT_NONE,
+                 stream=None):
+    """y = act(alpha * conv(x, w) + beta * C_res + bias) (tla_conv2d_fprop):
+    x NHWC, w KRSC, y and C_res NPQK, CUDA tensors of raw 16-bit storage."""
+    a = ConvArgs(N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1], dil[0], dil[1],
+                 _dev(x, "x"), _dev(w, "w"), _dev(C_res, "C_res"), _dev(y, "y"), dtype,
+                 _dev(bias, "bias"), bias_type if bias_type is not None else dtype, act,
+                 alpha, beta)
+    _check(lib().tla_conv2d_fprop(ctypes.byref(a), _stream(stream, x, w, y)), "tla_conv2d_fprop")
 
 
 GEMM_VARIANTS = 3

@@ -172,6 +172,38 @@ int tla_gemm_epilogue(const tla_gemm_args* args, void* stream) {
   return gemm_dispatch(p, (hipStream_t)stream, false, nullptr);
 }
 
+int tla_conv2d_fprop(const tla_conv2d_args* a, void* stream) {
+  if (!a) return TLA_ERR_INVALID_ARG;
+  if (a->N < 0 || a->H < 1 || a->W < 1 || a->C < 1 || a->K < 1 || a->R < 1 || a->S < 1)
+    return TLA_ERR_INVALID_ARG;
+  if (a->stride_h < 1 || a->stride_w < 1 || a->dil_h < 1 || a->dil_w < 1 || a->pad_h < 0 ||
+      a->pad_w < 0 || a->act < TLA_ACT_NONE || a->act > TLA_ACT_GELU)
+    return TLA_ERR_INVALID_ARG;
+  if (!is_out_type(a->type)) return TLA_ERR_UNSUPPORTED;
+  if (a->bias && !is_aux_type(a->bias_type)) return TLA_ERR_UNSUPPORTED;
+  const int64_t lim = int64_t(1) << 31;
+  if (a->H > lim || a->W > lim || a->R > lim || a->S > lim) return TLA_ERR_INVALID_ARG;
+  const int64_t ph = a->H + 2 * (int64_t)a->pad_h - (int64_t)a->dil_h * (a->R - 1) - 1;
+  const int64_t pw = a->W + 2 * (int64_t)a->pad_w - (int64_t)a->dil_w * (a->S - 1) - 1;
+  const int64_t P = ph < 0 ? 0 : ph / a->stride_h + 1, Q = pw < 0 ? 0 : pw / a->stride_w + 1;
+  if (a->N == 0 || P < 1 || Q < 1) return TLA_OK;
+  if (!a->x || !a->w || !a->y) return TLA_ERR_INVALID_ARG;
+  if (a->beta != 0.0f && !a->C_res) return TLA_ERR_INVALID_ARG;
+  if (a->N > lim / P || a->N * P > lim / Q || a->K >= lim || a->C > lim / (a->R * a->S) ||
+      a->R * a->S > lim || a->N * a->H > lim / a->W || a->N * a->H * a->W > lim / a->C)
+    return TLA_ERR_INVALID_ARG;
+  if (a->N * P * Q >= lim || a->R * a->S * a->C >= lim) return TLA_ERR_INVALID_ARG;
+  ConvProblem c{};
+  c.N = a->N; c.H = a->H; c.W = a->W; c.C_in = a->C; c.K = a->K; c.R = a->R; c.S = a->S;
+  c.P = P; c.Q = Q;
+  c.u = a->stride_h; c.v = a->stride_w; c.ph = a->pad_h; c.pw = a->pad_w;
+  c.dh = a->dil_h; c.dw = a->dil_w;
+  c.x = a->x; c.w = a->w; c.C = a->beta != 0.0f ? a->C_res : nullptr; c.y = a->y;
+  c.type = a->type; c.bias = a->bias; c.bias_type = a->bias ? a->bias_type : TLA_F32;
+  c.act = a->act; c.alpha = a->alpha; c.beta = a->beta;
+  return conv_dispatch(c, (hipStream_t)stream);
+}
+
 int tla_gemm_run_variant(const tla_gemm_args* args, int32_t variant, void* stream) {
   if (variant < 0 || variant >= kGemmVariants) return TLA_ERR_INVALID_ARG;
   GemmProblem p{};

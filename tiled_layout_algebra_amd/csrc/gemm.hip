@@ -31,6 +31,8 @@
 //   general any order, pitch or alignment, ragged K: registers staged through
 //           a strip-mined thread map with per-element predicates; elements
 //           outside the matrix load as zero.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "tla/copy.hpp"
 #include "tla/layout.hpp"
@@ -91,6 +93,10 @@ struct GemmParams {
   float alpha, beta;
   int tiles_m, tiles_n;
   int flags;
+  // implicit-GEMM convolution view of A (used by the kConv kernels only):
+  // image H x W x C (NHWC), filter R x S, output P x Q, stride (u, v),
+  // padding (ph, pw), dilation (dh, dw)
+  int cH, cW, cC, cR, cS, cP, cQ, cu, cv, cph, cpw, cdh, cdw;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -213,6 +219,65 @@ struct RegSlab {
       const int r = kcontig ? kmap.row(tid, it, 0) : rmap.row(tid, it, 0);
       const int c = kcontig ? kmap.col(tid, it, 0) : rmap.col(tid, it, 0);
       *(i32x4*)(slab + r * kRowBytes + Swz::chunk(r, c) * 16) = v[it];
+    }
+  }
+};
+
+// ---------------------------------------------- implicit-GEMM A loader
+// The A operand of a convolution seen as a GEMM (the implicit GEMM of the
+// PitchLinearStripminedThreadMap walk-through, section 5.2): row m is the
+// output pixel (n, p, q) = (m / PQ, m / Q mod P, m mod Q), column k the
+// filter position and channel (r, s, c) = (k / (S C), k / C mod S, k mod C),
+// and the element is x[n, p u - ph + r dh, q v - pw + s dw, c] -- zero outside
+// the image.  The slab is walked with the same row-contiguous strip-mined
+// map as a K-contiguous operand; when C is a multiple of the vector width
+// (and the image is 16-byte aligned) a 16-byte chunk never straddles a
+// filter position, so one bounds check covers it.
+template <int ROWS, int EB, int kRowBytes>
+struct ConvSlab : RegSlab<ROWS, EB, kRowBytes> {
+  using Base = RegSlab<ROWS, EB, kRowBytes>;
+
+  __device__ __forceinline__ const uint8_t* at(const GemmParams& p, int n, int h0, int w0,
+                                               int k) const {
+    const int c = k % p.cC, rs = k / p.cC;
+    const int r = rs / p.cS, s = rs - r * p.cS;
+    const int h = h0 + r * p.cdh, w = w0 + s * p.cdw;
+    if (h < 0 || h >= p.cH || w < 0 || w >= p.cW) return nullptr;
+    return p.A + ((((int64_t)n * p.cH + h) * p.cW + w) * p.cC + c) * EB;
+  }
+
+  __device__ __forceinline__ void load_conv(const GemmParams& p, int row0, int k0, bool vec_ok,
+                                            int tid) {
+    constexpr StripMinedMap kmap(ROWS, Base::kChunks, kThreads, 1, Base::kI, 1);
+    constexpr int kCE = Base::kCE;
+    const int PQ = p.cP * p.cQ;
+#pragma unroll
+    for (int it = 0; it < Base::kI; ++it) {
+      const int m = row0 + kmap.row(tid, it, 0);
+      const int k = k0 + kmap.col(tid, it, 0) * kCE;
+      i32x4 x = {0, 0, 0, 0};
+      if (m < p.M) {
+        const int n = m / PQ, pq = m - n * PQ, pp = pq / p.cQ, qq = pq - pp * p.cQ;
+        const int h0 = pp * p.cu - p.cph, w0 = qq * p.cv - p.cpw;
+        if (vec_ok && k + kCE <= p.K) {
+          const uint8_t* src = at(p, n, h0, w0, k);
+          if (src) x = *(const i32x4*)src;
+        } else {
+          uint8_t bytes[16] = {};
+#pragma unroll
+          for (int e = 0; e < kCE; ++e) {
+            if (k + e < p.K) {
+              const uint8_t* src = at(p, n, h0, w0, k + e);
+              if (src) {
+#pragma unroll
+                for (int b = 0; b < EB; ++b) bytes[e * EB + b] = src[b];
+              }
+            }
+          }
+          x = __builtin_bit_cast(i32x4, bytes);
+        }
+      }
+      this->v[it] = x;
     }
   }
 };
@@ -729,7 +794,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
 // kStages LDS stages of BM + BN rows of kRowBytes bytes each.  K-tile kt
 // lives in stage kt % kStages; up to kStages - 1 tiles are in flight, so the
 // copy of a tile has kStages - 1 tiles of matrix-core work to arrive in.
-template <int kCode, int BM, int BN, int kRowBytes, int kStages, bool kFast>
+template <int kCode, int BM, int BN, int kRowBytes, int kStages, bool kFast, bool kConv = false>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
   using Atom = MfmaAtom<kCode>;
   using Frag = typename Atom::Frag;
@@ -846,14 +911,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
               std::integral_constant<int, kMfmas>{});
       });
     };
-    RegSlab<BM, EB, kRowBytes> ra;
+    static_assert(!kConv || !kFast, "the convolution view uses the register-staged path");
+    std::conditional_t<kConv, ConvSlab<BM, EB, kRowBytes>, RegSlab<BM, EB, kRowBytes>> ra;
     RegSlab<BN, EB, kRowBytes> rb;
     const bool a_vec = (p.flags >> 8) & 1, b_vec = (p.flags >> 9) & 1;
     const bool a_kc = (p.a_sk == 1), b_kc = (p.b_sk == 1);
     if (KT > 0) {
-      ra.load(p.A, p.a_sr, p.a_sk, m0, p.M, 0, p.K, a_vec, tid);
+      if constexpr (kConv) ra.load_conv(p, m0, 0, a_vec, tid);
+      else ra.load(p.A, p.a_sr, p.a_sk, m0, p.M, 0, p.K, a_vec, tid);
       rb.load(p.B, p.b_sr, p.b_sk, n0, p.N, 0, p.K, b_vec, tid);
-      ra.store(smem, a_kc, tid);
+      ra.store(smem, kConv || a_kc, tid);
       rb.store(smem + SLAB_A, b_kc, tid);
     }
     __syncthreads();
@@ -861,12 +928,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
       uint8_t* cur = smem + (kt & 1) * STAGE;
       uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
       if (kt + 1 < KT) {
-        ra.load(p.A, p.a_sr, p.a_sk, m0, p.M, (kt + 1) * BK, p.K, a_vec, tid);
+        if constexpr (kConv) ra.load_conv(p, m0, (kt + 1) * BK, a_vec, tid);
+        else ra.load(p.A, p.a_sr, p.a_sk, m0, p.M, (kt + 1) * BK, p.K, a_vec, tid);
         rb.load(p.B, p.b_sr, p.b_sk, n0, p.N, (kt + 1) * BK, p.K, b_vec, tid);
       }
       compute(cur);
       if (kt + 1 < KT) {
-        ra.store(nxt, a_kc, tid);
+        ra.store(nxt, kConv || a_kc, tid);
         rb.store(nxt + SLAB_A, b_kc, tid);
       }
       __syncthreads();
@@ -971,6 +1039,51 @@ const void* variant_kernel(int v, int* threads) {
 }
 
 }  // namespace
+
+int conv_dispatch(const ConvProblem& c, hipStream_t stream) {
+  const int eb = elem_bytes(c.type);
+  GemmParams p{};
+  p.A = (const uint8_t*)c.x;
+  p.B = (const uint8_t*)c.w;
+  p.C = (const uint8_t*)c.C;
+  p.D = (uint8_t*)c.y;
+  p.bias = (const uint8_t*)c.bias;
+  p.M = (int)(c.N * c.P * c.Q);
+  p.N = (int)c.K;
+  p.K = (int)(c.R * c.S * c.C_in);
+  // B = the filter as K rows of R*S*C (K-contiguous); C and D are N*P*Q x K
+  p.b_sr = p.K;
+  p.b_sk = 1;
+  p.c_sm = p.d_sm = c.K;
+  p.c_sn = p.d_sn = 1;
+  p.c_type = p.d_type = c.type;
+  p.bias_type = c.bias_type;
+  p.act = c.act;
+  p.alpha = c.alpha;
+  p.beta = c.C ? c.beta : 0.f;
+  p.cH = (int)c.H; p.cW = (int)c.W; p.cC = (int)c.C_in; p.cR = (int)c.R; p.cS = (int)c.S;
+  p.cP = (int)c.P; p.cQ = (int)c.Q; p.cu = c.u; p.cv = c.v; p.cph = c.ph; p.cpw = c.pw;
+  p.cdh = c.dh; p.cdw = c.dw;
+  if (c.C && (c.K % 4) == 0 && aligned(c.C, 8)) p.flags |= kCVec;
+  if ((c.K % 4) == 0 && aligned(c.y, 8)) p.flags |= kDVec;
+  if (c.C && (c.K % 8) == 0 && aligned(c.C, 16)) p.flags |= kC16;
+  if ((c.K % 8) == 0 && aligned(c.y, 16)) p.flags |= kD16;
+  if (c.bias && aligned(c.bias, 4 * elem_bytes(c.bias_type))) p.flags |= kBiasVec;
+  const bool x_vec = (c.C_in * eb) % 16 == 0 && aligned(c.x, 16);
+  const bool w_vec = ((int64_t)p.K * eb) % 16 == 0 && aligned(c.w, 16);
+  p.flags |= (x_vec ? 1 << 8 : 0) | (w_vec ? 1 << 9 : 0);
+  int64_t grid;
+  set_grid(p, 128, 128, &grid);
+  if (grid <= 0) return TLA_OK;
+  if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
+  if (c.type == TLA_BF16)
+    hipLaunchKernelGGL((gemm_kernel<kBF16, 128, 128, 128, 2, false, true>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_kernel<kF16, 128, 128, 128, 2, false, true>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
+}
 
 int gemm_variant_info(int a_type, int variant, GemmKernelInfo* out) {
   if (variant < 0 || variant >= kGemmVariants) return TLA_ERR_INVALID_ARG;

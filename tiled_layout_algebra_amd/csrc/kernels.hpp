@@ -25,6 +25,19 @@ struct GemmProblem {
 
 // Picks the kernel variant; launches it unless `dry_run`.  `name` receives
 // the variant's name (may be NULL).
+// Forward convolution as an implicit GEMM: x N x H x W x C_in (NHWC), w K x
+// R x S x C_in (KRSC), y and C N x P x Q x K (NPQK); all of one 16-bit type.
+struct ConvProblem {
+  int64_t N, H, W, C_in, K, R, S, P, Q;
+  int u, v, ph, pw, dh, dw;
+  const void* x; const void* w; const void* C; void* y;
+  int type;
+  const void* bias; int bias_type;
+  int act;
+  float alpha, beta;
+};
+int conv_dispatch(const ConvProblem& c, hipStream_t stream);
+
 // GEMM kernel variants: 0 fast 256x256, 1 fast 128x128, 2 general 128x128.
 constexpr int kGemmVariants = 3;
 struct GemmKernelInfo {

@@ -272,3 +272,56 @@ class ThreadMapCase:
 
 
 THREAD_MAP_64x64 = ThreadMapCase(name="thread_map_64x64_t128_v4_i8", R=64, C=64, T=128, V=4, I=8)
+
+
+# ------------------------------------------------------------ convolution
+
+@dataclass
+class ConvCase:
+    """A forward convolution: x N x H x W x C (NHWC), w K x R x S x C (KRSC),
+    output N x P x Q x K (NPQK), all of one 16-bit type."""
+    name: str
+    N: int
+    H: int
+    W: int
+    C: int
+    K: int
+    R: int
+    S: int
+    stride: tuple = (1, 1)
+    pad: tuple = (0, 0)
+    dil: tuple = (1, 1)
+    dtype: int = F16
+    alpha: float = 1.0
+    beta: float = 0.0
+    act: int = ACT_NONE
+    has_c: bool = False
+    has_bias: bool = False
+    seed: int = 0
+    dist: str = "u1"          # x, w and C
+    dist_bias: str = "u01"
+    tol: float = 1e-2
+
+    def out_hw(self):
+        def one(extent, f, s, p, d):
+            span = extent + 2 * p - d * (f - 1) - 1
+            return 0 if span < 0 else span // s + 1
+        return (one(self.H, self.R, self.stride[0], self.pad[0], self.dil[0]),
+                one(self.W, self.S, self.stride[1], self.pad[1], self.dil[1]))
+
+
+def conv_inputs(case: ConvCase) -> dict:
+    """Seeded raw-bit inputs, drawn in the order x, w, C, bias."""
+    rng = np.random.default_rng(case.seed)
+    P, Q = case.out_hw()
+    x = encode(draw(rng, (case.N, case.H, case.W, case.C), case.dist), case.dtype)
+    w = encode(draw(rng, (case.K, case.R, case.S, case.C), case.dist), case.dtype)
+    c = encode(draw(rng, (case.N * P * Q, case.K), case.dist), case.dtype) if case.has_c else None
+    b = encode(draw(rng, (case.K,), case.dist_bias), case.dtype) if case.has_bias else None
+    return {"x": x, "w": w, "C": c, "bias": b}
+
+
+# A 3x3, stride-1, padded layer of 56 x 56 x 64 images (batch 32), fp16,
+# with bias and ReLU: an implicit GEMM of M = 100352, N = 64, K = 576.
+CONV_F16_56 = ConvCase(name="conv_f16_n32_56x56x64_k64_3x3", N=32, H=56, W=56, C=64, K=64, R=3,
+                       S=3, pad=(1, 1), dtype=F16, act=ACT_RELU, has_bias=True, seed=5)
