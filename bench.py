@@ -167,6 +167,20 @@ def hbm_traffic(prefix, kernel_file):
     return None
 
 
+def engine_clock(prefix, kernel_file):
+    """The engine clock (GHz) measured during `prefix`'s kernel, from
+    profiles/engine_clock.txt, or None when the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", "engine_clock.txt")
+    if not os.path.exists(path):
+        return None
+    sha = source_sha(kernel_file)
+    for line in open(path):
+        f = line.split()
+        if len(f) == 4 and f[0].startswith(prefix) and f[1] == sha:
+            return float(f[2])
+    return None
+
+
 def cpu_baseline(case, inp, target_s):
     """The oracle (unchanged) on the first R rows of the GEMM: R is grown
     until one run takes about target_s seconds; returns its TFLOP/s."""
@@ -275,6 +289,7 @@ def main():
     gemm_tflops = g.flops() / t_gemm.mean() / 1e12
     tr_gbs = tc.bytes_moved() / t_tr.mean() / 1e9
 
+    clk = engine_clock("gemm", "gemm.hip")
     out = {
         "metric": METRIC,
         "value": round(gemm_tflops, 2),
@@ -298,7 +313,12 @@ def main():
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": hbm_traffic("gemm", "gemm.hip"),
                      "kernel_us": round(t_gemm.mean() * 1e6, 2),
-                     "kernel_us_min": round(t_gemm.min() * 1e6, 2)},
+                     "kernel_us_min": round(t_gemm.min() * 1e6, 2),
+                     # the engine clock the counters saw during this kernel, and the
+                     # fraction of the MFMA peak at that clock (nameplate: 2.4 GHz)
+                     "clock_ghz": clk,
+                     "frac_at_clock": (round(gemm_tflops / (PEAK_BF16_TFLOPS * clk / 2.4), 4)
+                                       if clk else None)},
         "transpose": {"value": round(tr_gbs, 1), "unit": "GB/s",
                       "roofline": {"bound": "hbm", "achieved": round(tr_gbs, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
