@@ -4,7 +4,9 @@ against the direct-convolution oracle on the same seeded inputs.
 * integer-valued inputs: every partial sum is exact in fp32, so y must be
   the oracle's exact result rounded to y's type, bit for bit -- over stride,
   padding and dilation, channel counts that do and do not fill a 16-byte
-  vector, 1x1 and 5x5 filters, ragged output-channel and pixel counts;
+  vector or a whole 128-byte k-tile (the direct-to-LDS path, whose padding
+  taps read zeros from the buffer range check), 1x1 and 5x5 filters,
+  ragged output-channel and pixel counts;
 * random inputs with GELU within the tolerance, C aliasing y;
 * the measured layer (32 x 56 x 56 x 64, 3x3) compared in full.
 Tolerance: |y - ref| <= tol*(1 + |ref|), tol 1e-2.
@@ -50,6 +52,12 @@ GEOMETRIES = [  # N, H, W, C, K, R, S, stride, pad, dil
     (1, 17, 13, 24, 40, 5, 5, (2, 2), (2, 2), (1, 1)),
     (2, 12, 12, 32, 64, 3, 3, (1, 1), (2, 2), (2, 2)),
     (1, 6, 20, 40, 7, 2, 4, (3, 2), (0, 1), (1, 1)),
+    # channel counts that are multiples of 64 take the direct-to-LDS path
+    (2, 9, 11, 64, 24, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 10, 7, 128, 72, 3, 2, (2, 1), (1, 0), (1, 2)),
+    (3, 6, 6, 64, 130, 1, 1, (1, 1), (0, 0), (1, 1)),
+    (1, 17, 13, 64, 40, 5, 5, (2, 2), (2, 2), (1, 1)),
+    (2, 5, 7, 192, 33, 3, 3, (1, 2), (3, 3), (2, 1)),
 ]
 
 

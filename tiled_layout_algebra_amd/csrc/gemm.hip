@@ -593,10 +593,12 @@ __device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, 
 // per-lane 32-bit offset and uniform offset stay separate registers, so the
 // loop spends no vector instructions on copy addresses.  Every offset the
 // kernel forms is below 2^31 (checked by the host).
+// `records` bounds the buffer: a lane whose offset lies past it reads zeros
+// (the raw buffer range check) and touches no memory.
 __device__ __forceinline__ void dma16_buf(const uint8_t* base, uint32_t voffset, uint32_t soffset,
-                                          uint8_t* lds) {
+                                          uint8_t* lds, int records = 0x7FFFFFFF) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 0x7FFFFFFF, 0x00020000);
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, records, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset,
                                            soffset, 0, 0);
 #endif
@@ -624,7 +626,7 @@ __device__ __forceinline__ void dma16_buf(const uint8_t* base, uint32_t voffset,
 // below 32, so one base per k-step serves every 32-row fragment; grouping
 // the A slots and the B slots keeps every immediate below 64 KiB.
 template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront = 0, int kWM = 2,
-          int kWN = 2>
+          int kWN = 2, bool kConv = false>
 __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmParams p) {
   using Atom = MfmaAtom<kCode>;
   using Frag = typename Atom::Frag;
@@ -681,6 +683,26 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
     const int64_t rb = (kA ? p.a_sr : p.b_sr) * EB;
     off[q] = (uint32_t)(row * rb + Swz::chunk(r, tid % kChunks) * 16);
   });
+  // Implicit-GEMM convolution: A row m is the output pixel (n, p, q); a
+  // k-tile is 128 bytes of channels of one filter tap (C is a multiple of
+  // the tile), so the tap is uniform and each lane keeps its pixel's image
+  // origin (h0, w0) and byte offset.  Rows past M get an origin that no
+  // tap brings into the image.
+  int ch0[kConv ? IA : 1], cw0[kConv ? IA : 1];
+  if constexpr (kConv) {
+    static_for<IA>([&](auto q) {
+      const int m = m0 + tid / kChunks + (NT / kChunks) * q;
+      const int PQ = p.cP * p.cQ;
+      const int n = m / PQ, pq = m - n * PQ, pp = pq / p.cQ, qq = pq - pp * p.cQ;
+      const int h0 = pp * p.cu - p.cph, w0 = qq * p.cv - p.cpw;
+      const bool live = m < p.M;
+      ch0[q] = live ? h0 : -0x40000000;
+      cw0[q] = w0;
+      const int64_t base = (((int64_t)n * p.cH + h0) * p.cW + w0) * p.cC * EB;
+      off[q] = (uint32_t)(live ? base : 0) + Swz::chunk(tid / kChunks, tid % kChunks) * 16;
+    });
+  }
+  const int x_records = kConv ? (int)((int64_t)p.M / (p.cP * p.cQ) * p.cH * p.cW * p.cC * EB) : 0;
   // Fragment bases for each k-step (and each 16-byte half of a 32-byte
   // fragment): row wm0 + lane%32 of the A slot, wn0 + lane%32 of the B slot.
   uint32_t fa[KSTEPS][kSub], fb[KSTEPS][kSub];
@@ -715,7 +737,17 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
   // copy q of tile t into slot `slot`; tiles past K reload the last one
   auto copy = [&](int t, auto slot, auto q) {
     const uint32_t kb = (uint32_t)min(t, KT - 1) * kRowBytes;
-    if constexpr (q < IA)
+    if constexpr (q < IA && kConv) {
+      const int k0 = min(t, KT - 1) * BK;  // first channel of the tap, uniform
+      const int rs = k0 / p.cC, c0 = k0 - rs * p.cC;
+      const int fr = rs / p.cS, fs = rs - fr * p.cS;
+      const int dh = fr * p.cdh, dw = fs * p.cdw;
+      const int h = ch0[q] + dh, w = cw0[q] + dw;
+      const bool in = (unsigned)h < (unsigned)p.cH && (unsigned)w < (unsigned)p.cW;
+      const uint32_t tap = (uint32_t)(((dh * p.cW + dw) * p.cC + c0) * EB);
+      dma16_buf(p.A, in ? off[q] + tap : 0xFFFFFFF0u, 0,
+                smem + slot * SLAB_A + (wave * 64 + NT * q) * 16, x_records);
+    } else if constexpr (q < IA)
       dma16_buf(p.A, off[q], kb, smem + slot * SLAB_A + (wave * 64 + NT * q) * 16);
     else
       dma16_buf(p.B, off[q], kb, smem + B_BASE + slot * SLAB_B + (wave * 64 + NT * (q - IA)) * 16);
@@ -960,14 +992,15 @@ void set_grid(GemmParams& p, int BM, int BN, int64_t* grid) {
   *grid = (int64_t)p.tiles_m * p.tiles_n;
 }
 
-template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront, int kWM, int kWN>
+template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront, int kWM, int kWN,
+          bool kConv = false>
 int launch_fast(const GemmParams& p0, hipStream_t stream) {
   GemmParams p = p0;
   int64_t grid;
   set_grid(p, BM, BN, &grid);
   if (grid <= 0) return TLA_OK;
   if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((gemm_fast_kernel<kCode, BM, BN, kRowBytes, kStages, kFront, kWM, kWN>),
+  hipLaunchKernelGGL((gemm_fast_kernel<kCode, BM, BN, kRowBytes, kStages, kFront, kWM, kWN, kConv>),
                      dim3((unsigned)grid), dim3(64 * kWM * kWN), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
 }
@@ -1072,6 +1105,16 @@ int conv_dispatch(const ConvProblem& c, hipStream_t stream) {
   const bool x_vec = (c.C_in * eb) % 16 == 0 && aligned(c.x, 16);
   const bool w_vec = ((int64_t)p.K * eb) % 16 == 0 && aligned(c.w, 16);
   p.flags |= (x_vec ? 1 << 8 : 0) | (w_vec ? 1 << 9 : 0);
+  // Direct-to-LDS implicit GEMM when every 128-byte k-tile is channels of
+  // one tap (C a multiple of 64), 16-byte aligned image and filter rows and
+  // both operands below 2 GiB; otherwise the register-staged loader.
+  const int64_t x_bytes = c.N * c.H * c.W * c.C_in * eb;
+  const bool fast = (c.C_in * eb) % 128 == 0 && aligned(c.x, 16) && w_vec &&
+                    x_bytes < (int64_t(1) << 31) && (int64_t)p.K * p.N * eb < (int64_t(1) << 31);
+  if (fast) {
+    if (c.type == TLA_BF16) return launch_fast<kBF16, 128, 128, 128, 3, 1, 2, 2, true>(p, stream);
+    return launch_fast<kF16, 128, 128, 128, 3, 1, 2, 2, true>(p, stream);
+  }
   int64_t grid;
   set_grid(p, 128, 128, &grid);
   if (grid <= 0) return TLA_OK;
