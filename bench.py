@@ -101,10 +101,13 @@ def sweep(steps, warmup):
                                  "←" if info["name"] == auto else ""))
                 print(lines[-1], file=sys.stderr, flush=True)
             del dA, dB, dD
-    # implicit-GEMM convolution (register-staged general kernel, 128x128)
+    # implicit-GEMM convolution (direct-to-LDS kernel: C is a multiple of 64)
     lines += ["", "| convolution | N×H×W×C → K, R×S, stride, pad | GEMM M×N×K | µs | TFLOP/s "
               "| % peak |", "|---|---|---|---|---|---|"]
     for case in (W.CONV_F16_56,
+                 W.ConvCase(name="conv_f16_n32_56x56x128_k64_3x3", N=32, H=56, W=56, C=128,
+                            K=64, R=3, S=3, pad=(1, 1), dtype=W.F16, act=W.ACT_RELU,
+                            has_bias=True, seed=7),
                  W.ConvCase(name="conv_f16_n32_28x28x256_k256_3x3", N=32, H=28, W=28, C=256,
                             K=256, R=3, S=3, pad=(1, 1), dtype=W.F16, act=W.ACT_RELU,
                             has_bias=True, seed=6)):

@@ -5,8 +5,9 @@ against the direct-convolution oracle on the same seeded inputs.
   the oracle's exact result rounded to y's type, bit for bit -- over stride,
   padding and dilation, channel counts that do and do not fill a 16-byte
   vector or a whole 128-byte k-tile (the direct-to-LDS path, whose padding
-  taps read zeros from the buffer range check), 1x1 and 5x5 filters,
-  ragged output-channel and pixel counts;
+  taps read zeros from the buffer range check; 256 x 64 tiles up to 64
+  output channels, 128 x 128 above), 1x1 and 5x5 filters, ragged
+  output-channel and pixel counts, whole tiles through the LDS epilogue;
 * random inputs with GELU within the tolerance, C aliasing y;
 * the measured layer (32 x 56 x 56 x 64, 3x3) compared in full.
 Tolerance: |y - ref| <= tol*(1 + |ref|), tol 1e-2.
@@ -58,6 +59,11 @@ GEOMETRIES = [  # N, H, W, C, K, R, S, stride, pad, dil
     (3, 6, 6, 64, 130, 1, 1, (1, 1), (0, 0), (1, 1)),
     (1, 17, 13, 64, 40, 5, 5, (2, 2), (2, 2), (1, 1)),
     (2, 5, 7, 192, 33, 3, 3, (1, 2), (3, 3), (2, 1)),
+    # 64 output channels: whole 256 x 64 tiles (and a ragged last one);
+    # 128 output channels: whole 128 x 128 tiles -- the LDS epilogue with C
+    (4, 16, 16, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (3, 9, 10, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (2, 8, 16, 128, 128, 3, 3, (1, 1), (1, 1), (1, 1)),
 ]
 
 
