@@ -177,7 +177,8 @@ int tla_tiled_transpose(const void *src, int64_t ld_src, void *dst, int64_t ld_d
  * (length K, f16/bf16/f32) may be NULL; C may be NULL when beta == 0 and may
  * alias y.  P = (H + 2 ph - dh (R-1) - 1) / u + 1 and Q likewise (floor).
  * The GEMM has M = N*P*Q, N = K, K = R*S*C; each of them must stay below
- * 2^31.  N == 0, P < 1 or Q < 1 is a no-op.  Strides and dilations must be
+ * 2^31, and so must N*H*W*C; the padded extents H + 2 ph and W + 2 pw must
+ * stay below 2^30.  N == 0, P < 1 or Q < 1 is a no-op.  Strides and dilations must be
  * >= 1, paddings >= 0, extents >= 1 (TLA_ERR_INVALID_ARG otherwise).
  */
 typedef struct {

@@ -230,6 +230,8 @@ def _conv(**kw):
     (dict(pad_h=-1), tla.ERR_INVALID_ARG), (dict(act=9), tla.ERR_INVALID_ARG),
     (dict(type=tla.E4M3), tla.ERR_UNSUPPORTED), (dict(x=None), tla.ERR_INVALID_ARG),
     (dict(beta=0.5), tla.ERR_INVALID_ARG),                       # beta != 0 without C
+    (dict(pad_h=1 << 29, stride_h=1 << 30), tla.ERR_INVALID_ARG),  # padded extent >= 2^30
+    (dict(W=(1 << 30) - 2, pad_w=1, N=0), tla.ERR_INVALID_ARG),
     (dict(N=0), tla.OK), (dict(H=2, R=5, pad_h=0), tla.OK),     # empty output: no-op
 ])
 def test_conv_argument_errors(kw, status):

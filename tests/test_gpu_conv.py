@@ -64,6 +64,10 @@ GEOMETRIES = [  # N, H, W, C, K, R, S, stride, pad, dil
     (4, 16, 16, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
     (3, 9, 10, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
     (2, 8, 16, 128, 128, 3, 3, (1, 1), (1, 1), (1, 1)),
+    # coordinates near 2^20 (padding, stride and dilation): taps on both sides
+    # of the image, tap byte offsets that pass 2^32 on the direct-to-LDS path
+    (2, 5, 32, 64, 24, 3, 1, (2**20 + 3, 1), (2**20, 0), (2**19, 1)),
+    (2, 5, 32, 16, 24, 3, 1, (2**20 + 3, 1), (2**20, 0), (2**19, 1)),
 ]
 
 

@@ -183,6 +183,10 @@ int tla_conv2d_fprop(const tla_conv2d_args* a, void* stream) {
   if (a->bias && !is_aux_type(a->bias_type)) return TLA_ERR_UNSUPPORTED;
   const int64_t lim = int64_t(1) << 31;
   if (a->H > lim || a->W > lim || a->R > lim || a->S > lim) return TLA_ERR_INVALID_ARG;
+  // padded extents below 2^30 keep every image coordinate the kernels form
+  // (p*u - ph + r*dh and the like) inside a 32-bit int
+  if (a->H + 2 * (int64_t)a->pad_h >= (lim >> 1) || a->W + 2 * (int64_t)a->pad_w >= (lim >> 1))
+    return TLA_ERR_INVALID_ARG;
   const int64_t ph = a->H + 2 * (int64_t)a->pad_h - (int64_t)a->dil_h * (a->R - 1) - 1;
   const int64_t pw = a->W + 2 * (int64_t)a->pad_w - (int64_t)a->dil_w * (a->S - 1) - 1;
   const int64_t P = ph < 0 ? 0 : ph / a->stride_h + 1, Q = pw < 0 ? 0 : pw / a->stride_w + 1;

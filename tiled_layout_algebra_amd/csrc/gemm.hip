@@ -745,7 +745,10 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
       const int dh = fr * p.cdh, dw = fs * p.cdw;
       const int h = ch0[q] + dh, w = cw0[q] + dw;
       const bool in = (unsigned)h < (unsigned)p.cH && (unsigned)w < (unsigned)p.cW;
-      const uint32_t tap = (uint32_t)(((dh * p.cW + dw) * p.cC + c0) * EB);
+      // modulo 2^32, like off[q]: their sum is the tap's true offset (below
+      // 2^31) whenever the tap is inside the image
+      const uint32_t tap = (((uint32_t)dh * (uint32_t)p.cW + (uint32_t)dw) * (uint32_t)p.cC +
+                            (uint32_t)c0) * (uint32_t)EB;
       dma16_buf(p.A, in ? off[q] + tap : 0xFFFFFFF0u, 0,
                 smem + slot * SLAB_A + (wave * 64 + NT * q) * 16, x_records);
     } else if constexpr (q < IA)
