@@ -9,7 +9,8 @@ against the direct-convolution oracle on the same seeded inputs.
   output channels, 128 x 128 above), 1x1 and 5x5 filters, ragged
   output-channel and pixel counts, whole tiles through the LDS epilogue;
 * random inputs with GELU within the tolerance, C aliasing y;
-* the measured layer (32 x 56 x 56 x 64, 3x3) compared in full.
+* the measured layer (32 x 56 x 56 x 64, 3x3) compared in full, and the
+  32 x 28 x 28 x 256 layer on sampled outputs.
 Tolerance: |y - ref| <= tol*(1 + |ref|), tol 1e-2.
 """
 import numpy as np
@@ -104,3 +105,26 @@ def test_measured_layer_full():
     case = W.CONV_F16_56
     inp = W.conv_inputs(case)
     _tolerance(case, _run(case, inp), _oracle(case, inp))
+
+
+def test_wide_layer_sampled():
+    """32 x 28 x 28 x 256 -> 256 (3x3, pad 1, bias, ReLU), the 128 x 128 tile
+    path at full size: every tile-boundary row and column plus random points
+    against the oracle's per-point mode."""
+    case = W.ConvCase(name="conv_f16_n32_28x28x256_k256_3x3", N=32, H=28, W=28, C=256, K=256,
+                      R=3, S=3, pad=(1, 1), dtype=W.F16, act=W.ACT_RELU, has_bias=True, seed=6)
+    inp = W.conv_inputs(case)
+    got = _run(case, inp)
+    M = got.shape[0]
+    rng = np.random.default_rng(11)
+    edges_m = np.unique(np.clip(np.concatenate([np.arange(0, M, 128), np.arange(127, M, 128)]),
+                                0, M - 1))
+    edges_k = np.array([0, 63, 64, 127, 128, 255])
+    ms = np.concatenate([np.repeat(edges_m, edges_k.size), rng.integers(0, M, 4096)])
+    ks = np.concatenate([np.tile(edges_k, edges_m.size), rng.integers(0, case.K, 4096)])
+    ref = oc.conv2d_points(ms, ks, inp["x"], inp["w"], case.N, case.H, case.W, case.C, case.K,
+                           case.R, case.S, case.stride, case.pad, case.dil, case.dtype,
+                           bias=inp["bias"], bias_type=case.dtype, alpha=case.alpha,
+                           beta=case.beta, act=case.act)
+    ok, worst = og.within_tolerance(og.decode(case.dtype, got[ms, ks]), ref, case.tol)
+    assert ok, "worst |y-ref|/(1+|ref|) = %g" % worst
