@@ -10,7 +10,10 @@ Prints ONE JSON line.  `value` is the GEMM's TFLOP/s (2*M*N*K useful flops
 per launch over its average launch time, measured with HIP events recorded
 on the launch stream); the transpose's GB/s (algorithmic bytes: one read and
 one write of the matrix) is reported beside it, each with its roofline.
-`cpu_baseline` times the oracle on a bounded row sample of the same GEMM.
+After the step loop the e4m3 8192^3 + GELU GEMM ("fp8", against the fp8
+peak) and the fp16 256^3 GEMM ("f16_256") are timed on their own.
+`cpu_baseline` times the oracle on a bounded row sample of the bf16 GEMM
+(and of the fp8 GEMM and the transpose, inside their entries).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --sweep [--steps K] [--warmup W]   # GEMM variant x shape table
@@ -27,7 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "bf16 GEMM+epilogue TFLOP/s @4096³ (% MFMA peak); transpose GB/s (% HBM peak)"
-PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz, dense (fp16 the same)
+PEAK_FP8_TFLOPS = 5033.2    # twice the 16-bit rate, dense
 PEAK_HBM_GBS = 8000.0
 
 
@@ -39,6 +43,8 @@ def parse():
     # 5 warm-up steps timed the GEMM at 119.7 us, 50 at 112.9, 200 at 111.5
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the separately timed fp8 8192^3 and fp16 256^3 GEMMs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -59,7 +65,7 @@ def sweep(steps, warmup):
     import torch
     import tiled_layout_algebra_amd as tla
     import workloads as W
-    from tests.gpu_util import to_dev
+    from workloads.device import to_dev
 
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
@@ -196,7 +202,8 @@ def cpu_baseline(case, inp, target_s):
         kw = dict(M=rows, N=case.N, K=case.K, A=inp["A"][: rows * case.lda], a_type=case.a_type,
                   a_order=case.a_order, lda=case.lda, B=inp["B"], b_type=case.b_type,
                   b_order=case.b_order, ldb=case.ldb,
-                  C=inp["C"][: rows * case.ldc], c_type=case.c_type, c_order=case.c_order,
+                  C=None if inp["C"] is None else inp["C"][: rows * case.ldc],
+                  c_type=case.c_type, c_order=case.c_order,
                   ldc=case.ldc, bias=inp["bias"], bias_type=case.bias_type, alpha=case.alpha,
                   beta=case.beta, act=case.act, nthreads=threads)
         t0 = time.perf_counter()
@@ -207,8 +214,86 @@ def cpu_baseline(case, inp, target_s):
         rows = min(case.M, max(rows * 2, int(rows * target_s / max(dt, 1e-3))))
     flops = 2.0 * rows * case.N * case.K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d of %d output rows of the bf16 4096^3 GEMM+epilogue (all %d "
-                      "columns, full K); %.1f s" % (rows, case.M, case.N, dt)}
+            "sample": "first %d of %d output rows of %s (all %d columns, full K); %.1f s"
+                      % (rows, case.M, case.name, case.N, dt)}
+
+
+def cpu_baseline_transpose(tc, src, target_s):
+    """The oracle's bit-copy transpose (one host thread) on the first R source
+    rows of the matrix, R grown until one run takes about target_s seconds;
+    returns its GB/s of algorithmic bytes (one read and one write)."""
+    from oracle import gemm as og
+    rows = 64
+    while True:
+        sub = src[: rows * tc.ld_src]
+        t0 = time.perf_counter()
+        og.transpose(sub, rows, tc.N, tc.ld_src, rows)
+        dt = time.perf_counter() - t0
+        if dt >= target_s * 0.5 or rows >= tc.M:
+            break
+        rows = min(tc.M, max(rows * 2, int(rows * target_s / max(dt, 1e-3))))
+    return {"value": 2.0 * rows * tc.N * tc.elem_bytes / dt / 1e9, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "first %d of %d source rows of the fp32 %dx%d transpose; %.1f s"
+                      % (rows, tc.M, tc.M, tc.N, dt)}
+
+
+def time_launches(fn, stream, warmup, steps):
+    """Per-launch seconds of `fn` from HIP events recorded on `stream` around
+    each launch, after `warmup` untimed launches."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e-3
+
+
+def gemm_call(tla, case, dA, dB, dD, dC, dbias, stream):
+    def run():
+        tla.gemm_epilogue(case.M, case.N, case.K, dA, case.a_type, case.a_order, case.lda, dB,
+                          case.b_type, case.b_order, case.ldb, dD, case.d_type, case.d_order,
+                          case.ldd, C=dC, c_type=case.c_type, c_order=case.c_order, ldc=case.ldc,
+                          bias=dbias, bias_type=case.bias_type, alpha=case.alpha, beta=case.beta,
+                          scale_a=case.scale_a, scale_b=case.scale_b, act=case.act,
+                          stream=stream.cuda_stream)
+    return run
+
+
+def extra_gemm(tla, W, case, peak, stream, warmup, steps, cpu_s):
+    """One of the other measured GEMMs, timed on its own after the step loop:
+    TFLOP/s against `peak`, and (cpu_s > 0) the oracle on a row sample."""
+    import torch
+    from workloads.device import to_dev
+    inp = W.gemm_inputs(case)
+    dA, dB = to_dev(inp["A"]), to_dev(inp["B"])
+    dC = to_dev(inp["C"]) if inp["C"] is not None else None
+    dbias = to_dev(inp["bias"]) if inp["bias"] is not None else None
+    dD = torch.empty(case.M * case.ldd, dtype=torch.int16, device="cuda")
+    run = gemm_call(tla, case, dA, dB, dD, dC, dbias, stream)
+    t = time_launches(run, stream, warmup, steps)
+    tf = case.flops() / t.mean() / 1e12
+    out = {"workload": case.name, "variant": tla.gemm_variant(
+               case.M, case.N, case.K, dA, case.a_type, case.a_order, case.lda, dB, case.b_type,
+               case.b_order, case.ldb, dD, case.d_type, case.d_order, case.ldd, C=dC,
+               c_type=case.c_type, ldc=case.ldc, bias=dbias, bias_type=case.bias_type,
+               alpha=case.alpha, beta=case.beta, scale_a=case.scale_a, scale_b=case.scale_b,
+               act=case.act),
+           "value": round(tf, 2), "unit": "TFLOP/s",
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+                        "kernel_us": round(t.mean() * 1e6, 2),
+                        "kernel_us_min": round(t.min() * 1e6, 2)}}
+    if cpu_s > 0:
+        out["cpu_baseline"] = cpu_baseline(case, inp, cpu_s)
+    del dA, dB, dC, dbias, dD
+    return out
 
 
 def main():
@@ -224,7 +309,7 @@ def main():
     import torch
     import tiled_layout_algebra_amd as tla
     import workloads as W
-    from tests.gpu_util import to_dev
+    from workloads.device import to_dev
 
     torch.cuda.set_device(0)
     g = W.GEMM_BF16_4096
@@ -332,8 +417,19 @@ def main():
                                    "kernel_us": round(t_tr.mean() * 1e6, 2),
                                    "kernel_us_min": round(t_tr.min() * 1e6, 2)}},
     }
+    # The other two measured GEMMs, each timed on its own after the step loop
+    # (not part of a step): the fp8 8192^3 + GELU against the fp8 peak, and
+    # the launch-bound fp16 256^3.
+    if not args.no_extra:
+        cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds / 3
+        out["fp8"] = extra_gemm(tla, W, W.GEMM_E4M3_8192, PEAK_FP8_TFLOPS, stream, args.warmup,
+                                K, cpu_s)
+        out["f16_256"] = extra_gemm(tla, W, W.GEMM_F16_256, PEAK_BF16_TFLOPS, stream,
+                                    args.warmup, K, 0.0)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(g, inp, args.cpu_seconds)
+        out["transpose"]["cpu_baseline"] = cpu_baseline_transpose(
+            tc, W.transpose_input(tc), args.cpu_seconds / 3)
     print(json.dumps(out), flush=True)
 
 

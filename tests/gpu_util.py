@@ -6,27 +6,7 @@ import torch
 import tiled_layout_algebra_amd as tla
 import workloads as W
 from oracle import gemm as og
-
-_TORCH = {np.dtype(np.uint8): torch.uint8, np.dtype(np.uint16): torch.int16,
-          np.dtype(np.uint32): torch.int32, np.dtype(np.uint64): torch.int64}
-_NP_SIGNED = {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32,
-              np.dtype(np.uint64): np.int64, np.dtype(np.uint8): np.uint8}
-
-
-def to_dev(a: np.ndarray, pad_front: int = 0) -> torch.Tensor:
-    """Copy raw bits to the GPU; pad_front extra elements in front shift the
-    data off the allocation's alignment (the returned view starts there)."""
-    a = np.ascontiguousarray(a)
-    flat = a.reshape(-1).view(_NP_SIGNED[a.dtype])
-    t = torch.empty(flat.size + pad_front, dtype=_TORCH[a.dtype], device="cuda")
-    if pad_front:
-        t[:pad_front] = 0
-    t[pad_front:].copy_(torch.from_numpy(flat.copy()))
-    return t[pad_front:]
-
-
-def to_host(t: torch.Tensor, like: np.dtype) -> np.ndarray:
-    return t.cpu().numpy().view(like)
+from workloads.device import to_dev, to_host  # noqa: F401  (re-exported for the tests)
 
 
 def run_gemm(case: W.GemmCase, inp: dict, sentinel=None, pad_front=0, d_is_c=False, variant=None):
