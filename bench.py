@@ -17,6 +17,7 @@ peak) and the fp16 256^3 GEMM ("f16_256") are timed on their own.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --sweep [--steps K] [--warmup W]   # GEMM variant x shape table
+    python bench.py --variants [--steps K] [--warmup W]  # big GEMMs, each fast variant
 """
 import argparse
 import json
@@ -50,6 +51,12 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="append a plain 1 GiB device-to-device copy to every step (a kernel "
                          "of known traffic, for scaling HBM byte counters)")
+    ap.add_argument("--variants", action="store_true",
+                    help="instead of the JSON line: run the bf16 4096^3 and e4m3 8192^3 "
+                         "workloads with every fast GEMM variant forced (a short program "
+                         "for profiler counter passes) and print one line per variant")
+    ap.add_argument("--pad", type=int, default=0,
+                    help="with --variants: extra elements on every leading dimension")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the JSON line: time every compiled GEMM variant on a "
                          "set of shapes and print a table with each kernel's occupancy")
@@ -149,13 +156,17 @@ def sweep(steps, warmup):
 
 CSRC = os.path.join(ROOT, "tiled_layout_algebra_amd", "csrc")
 _HEADERS = ["tla/layout.hpp", "tla/copy.hpp", "tla/mfma.hpp", "kernels.hpp"]
+# the sources each measured kernel is built from, besides _HEADERS
+GEMM_SOURCES = "gemm_pingpong.hip+gemm_common.hpp"
+TRANSPOSE_SOURCES = "transpose.hip"
 
 
-def source_sha(kernel_file):
-    """First 16 hex digits of sha256 over a kernel source and the shared headers."""
+def source_sha(kernel_files):
+    """First 16 hex digits of sha256 over a kernel's sources ('+'-separated
+    names under csrc/) followed by the shared headers."""
     import hashlib
     h = hashlib.sha256()
-    for f in [kernel_file] + _HEADERS:
+    for f in kernel_files.split("+") + _HEADERS:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -296,6 +307,51 @@ def extra_gemm(tla, W, case, peak, stream, warmup, steps, cpu_s):
     return out
 
 
+def variants(steps, warmup, pad=0):
+    """The two large measured GEMMs with each fast variant forced: per-launch
+    µs from HIP events, one line per (workload, variant).  pad > 0 adds that
+    many elements to every leading dimension (same math, other addresses)."""
+    import dataclasses
+    import torch
+    import tiled_layout_algebra_amd as tla
+    import workloads as W
+    from workloads.device import to_dev
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    for case, peak in ((W.GEMM_BF16_4096, PEAK_BF16_TFLOPS), (W.GEMM_E4M3_8192, PEAK_FP8_TFLOPS)):
+        if pad:
+            case = dataclasses.replace(case, name=case.name + "_pad%d" % pad, lda=case.lda + pad,
+                                       ldb=case.ldb + pad, ldc=case.ldc + pad if case.has_c else 0,
+                                       ldd=case.ldd + pad)
+        inp = W.gemm_inputs(case)
+        dA, dB = to_dev(inp["A"]), to_dev(inp["B"])
+        dC = to_dev(inp["C"]) if inp["C"] is not None else None
+        dbias = to_dev(inp["bias"]) if inp["bias"] is not None else None
+        dD = torch.empty(case.M * case.ldd, dtype=torch.int16, device="cuda")
+        # three rounds, variants alternating, so clock drift hits all alike
+        times = {}
+        for rnd in range(3):
+            for v in (0, 3, 1):
+                def run():
+                    tla.gemm_epilogue(case.M, case.N, case.K, dA, case.a_type, case.a_order,
+                                      case.lda, dB, case.b_type, case.b_order, case.ldb, dD,
+                                      case.d_type, case.d_order, case.ldd, C=dC,
+                                      c_type=case.c_type, c_order=case.c_order, ldc=case.ldc,
+                                      bias=dbias, bias_type=case.bias_type, alpha=case.alpha,
+                                      beta=case.beta, scale_a=case.scale_a, scale_b=case.scale_b,
+                                      act=case.act, stream=stream.cuda_stream, variant=v)
+                t = time_launches(run, stream, warmup if rnd == 0 else 2, steps)
+                times.setdefault(v, []).append(t.mean())
+        for v in (0, 3, 1):
+            name = tla.gemm_variant_info(v, case.a_type)["name"]
+            us = float(np.median(times[v])) * 1e6
+            tf = case.flops() / (us * 1e-6) / 1e12
+            print("%s %s %.1f us (rounds: %s) %.0f TFLOP/s %.3f of peak" % (
+                case.name, name, us, " ".join("%.1f" % (x * 1e6) for x in times[v]), tf, tf / peak),
+                flush=True)
+        del dA, dB, dC, dbias, dD
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -304,6 +360,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(max(args.steps, 1), args.warmup)
+        return
+    if args.variants:
+        variants(max(args.steps, 1), args.warmup, args.pad)
         return
 
     import torch
@@ -379,7 +438,7 @@ def main():
     gemm_tflops = g.flops() / t_gemm.mean() / 1e12
     tr_gbs = tc.bytes_moved() / t_tr.mean() / 1e9
 
-    clk = engine_clock("gemm", "gemm.hip")
+    clk = engine_clock("gemm", GEMM_SOURCES)
     out = {
         "metric": METRIC,
         "value": round(gemm_tflops, 2),
@@ -401,7 +460,7 @@ def main():
                    "transpose": {"M": tc.M, "N": tc.N, "elem_bytes": 4, "seed": tc.seed}},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": hbm_traffic("gemm", "gemm.hip"),
+                     "traffic": hbm_traffic("gemm", GEMM_SOURCES),
                      "kernel_us": round(t_gemm.mean() * 1e6, 2),
                      "kernel_us_min": round(t_gemm.min() * 1e6, 2),
                      # the engine clock the counters saw during this kernel, and the
@@ -413,7 +472,7 @@ def main():
                       "roofline": {"bound": "hbm", "achieved": round(tr_gbs, 1),
                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": round(tr_gbs / PEAK_HBM_GBS, 4),
-                                   "traffic": hbm_traffic("transpose", "transpose.hip"),
+                                   "traffic": hbm_traffic("transpose", TRANSPOSE_SOURCES),
                                    "kernel_us": round(t_tr.mean() * 1e6, 2),
                                    "kernel_us_min": round(t_tr.min() * 1e6, 2)}},
     }

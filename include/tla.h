@@ -122,21 +122,27 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  * Tile-configuration dispatch ("CUTLASS / CuTe 主线", the kernel-composition
  * and profiling lesson; the ThreadblockShape trade-off between reuse and
  * occupancy).  The library compiles TLA_GEMM_VARIANTS kernels:
- *   0 "gemm_fast_256x256"    256x256 tiles (16-bit: 8 wavefronts;
- *                            e4m3: 4), direct global->LDS copies
- *   1 "gemm_fast_128x128"    128x128 tiles, 4 wavefronts, direct copies
- *   2 "gemm_general_128x128" 128x128 tiles, register-staged predicated
- *                            loads: any order, pitch, alignment, ragged K
+ *   0 "gemm_pingpong_256x256" 256x256 tiles, 8 wavefronts in two groups of
+ *                            four (2x2 waves of 64x128 each) that take turns
+ *                            between MFMA-only and memory phases; direct
+ *                            global->LDS copies; every operand type
+ *   1 "gemm_fast_128x128"    128x128 tiles, direct copies (16-bit: 8
+ *                            wavefronts of 64x32; e4m3: 4 of 64x64)
+ *   2 "gemm_general_128x128" 128x128 tiles, 4 wavefronts, register-staged
+ *                            predicated loads: any order, pitch, alignment,
+ *                            ragged K
+ *   3 "gemm_fast_256x256"    256x256 tiles, one group (16-bit: 8 wavefronts
+ *                            of 128x64; e4m3: 4 of 128x128), direct copies
  * tla_gemm_epilogue picks one from the problem: in the fast layout,
- * variant 0 for 16-bit operands with at least 128 tiles of 256x256 and 1
- * otherwise (e4m3 always 1, measured faster); variant 2 outside it;
+ * variant 0 with at least 128 tiles of 256x256 and 1 otherwise; variant 2
+ * outside it;
  * tla_gemm_run_variant runs the one asked for, with the same semantics and
  * tolerance, or returns TLA_ERR_UNSUPPORTED when a fast variant is asked
  * for a problem without the fast layout (both operands K-contiguous,
  * 16-byte aligned rows, K a multiple of 128 bytes, each operand < 2 GiB).
  * Variant ids outside [0, TLA_GEMM_VARIANTS) are TLA_ERR_INVALID_ARG.
  */
-#define TLA_GEMM_VARIANTS 3
+#define TLA_GEMM_VARIANTS 4
 int tla_gemm_run_variant(const tla_gemm_args *args, int32_t variant, void *stream);
 
 /* A variant's compiled kernel for operand type a_type, as the HIP runtime

@@ -92,10 +92,11 @@ def test_gemm_null_args_and_noops():
 
 def test_gemm_variant_choice():
     # aligned K-contiguous operands with K a multiple of the slab width: fast
-    assert _variant(_args(M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldd=4096))[1] == "gemm_fast_256x256"
+    assert _variant(_args(M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldd=4096))[1] == "gemm_pingpong_256x256"
     assert _variant(_args(M=256, N=256, K=256, lda=256, ldb=256, ldd=256))[1] == "gemm_fast_128x128"
     e4 = dict(a_type=tla.E4M3, b_type=tla.E4M3, M=8192, N=8192, K=8192, lda=8192, ldb=8192, ldd=8192)
-    assert _variant(_args(**e4))[1] == "gemm_fast_128x128"  # e4m3: measured faster
+    assert _variant(_args(**e4))[1] == "gemm_pingpong_256x256"
+    assert _variant(_args(**dict(e4, M=1024, N=1024)))[1] == "gemm_fast_128x128"
     # fp8 slabs are 128 elements wide: K = 64 is ragged for e4m3
     assert _variant(_args(**dict(e4, K=64, lda=64, ldb=64)))[1] == "gemm_general_128x128"
     # N-contiguous B, odd pitches, misaligned bases, ragged K: general
@@ -209,10 +210,10 @@ def test_run_variant_argument_errors():
     fast variant on a problem without the fast layout is refused -- both
     before any device work."""
     a = _args()
-    for bad in (-1, 3, 99):
+    for bad in (-1, tla.GEMM_VARIANTS, 99):
         assert tla.lib().tla_gemm_run_variant(ctypes.byref(a), bad, None) == tla.ERR_INVALID_ARG
     nn = _args(b_order=tla.ROW_MAJOR, ldb=64)
-    for v in (0, 1):
+    for v in (0, 1, 3):
         assert tla.lib().tla_gemm_run_variant(ctypes.byref(nn), v, None) == tla.ERR_UNSUPPORTED
 
 

@@ -120,10 +120,12 @@ def test_bf16_epilogue_reduced_full():
 
 
 def test_bf16_fast256_ragged_edges():
-    # 8 x 16 tiles of 256 take the 256x256 fast path; M and N end mid-tile
+    # 8 x 16 tiles of 256 take the two-group 256x256 kernel; M and N end
+    # mid-tile (M = 7*256 + 208: the last tile's rows end inside a 32-row
+    # copy block, whose missing rows load as zeros)
     case = dataclasses.replace(W.GEMM_BF16_4096, M=2000, N=4000, K=256, lda=0, ldb=0, ldc=0, ldd=0)
     case.__post_init__()
-    assert G.variant(case) == "gemm_fast_256x256"
+    assert G.variant(case) == "gemm_pingpong_256x256"
     _check_full(case, W.gemm_inputs(case))
 
 
@@ -140,7 +142,7 @@ def e4m3_8192_inputs():
 def test_bf16_4096_full_size_sampled(bf16_4096_inputs):
     """Fast pre-check: every tile-boundary row and column plus random points."""
     case = W.GEMM_BF16_4096
-    assert G.variant(case) == "gemm_fast_256x256"
+    assert G.variant(case) == "gemm_pingpong_256x256"
     _check_sampled(case, bf16_4096_inputs)
 
 
@@ -148,7 +150,7 @@ def test_bf16_4096_full_size_every_output(bf16_4096_inputs):
     """The verdict at full size: all 4096 x 4096 outputs against the whole
     oracle GEMM, within 1e-2 (1 + |ref|), no NaN, D's padding untouched."""
     case = W.GEMM_BF16_4096
-    assert G.variant(case) == "gemm_fast_256x256"
+    assert G.variant(case) == "gemm_pingpong_256x256"
     _check_full(case, bf16_4096_inputs)
 
 
@@ -272,7 +274,7 @@ def test_fast_path_pitched_at_scale():
     whole-row LDS epilogue read and write through the pitch."""
     case = _small(M=4096, N=4096, K=1024, act=W.ACT_RELU, seed=21)
     case.lda, case.ldb, case.ldc, case.ldd = 1024 + 64, 1024 + 8, 4096 + 8, 4096 + 24
-    assert G.variant(case) == "gemm_fast_256x256"
+    assert G.variant(case) == "gemm_pingpong_256x256"
     _check_sampled(case, W.gemm_inputs(case), seed=3)
 
 
@@ -288,7 +290,7 @@ def test_general_path_pitched_at_scale():
 
 # ------------------------------------------------- tile-configuration dispatch
 
-@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 @pytest.mark.parametrize("a_type,d_type", [(W.BF16, W.BF16), (W.F16, W.F16), (W.E4M3, W.BF16)])
 def test_forced_variants_bit_exact(variant, a_type, d_type):
     """Every compiled variant, forced through tla_gemm_run_variant on the
@@ -306,7 +308,7 @@ def test_forced_variants_bit_exact(variant, a_type, d_type):
     assert np.array_equal(W.d_logical(case, D), want)
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 def test_forced_variants_random_inputs(variant):
     case = _small(M=640, N=768, K=512, act=W.ACT_GELU, seed=92)
     _check_full(case, W.gemm_inputs(case), variant=variant)
@@ -315,7 +317,7 @@ def test_forced_variants_random_inputs(variant):
 def test_forced_fast_variant_refuses_general_layout():
     import tiled_layout_algebra_amd as tla
     case = _small(b_order=W.ROW)  # B N-contiguous: no fast layout
-    for variant in (0, 1):
+    for variant in (0, 1, 3):
         with pytest.raises(tla.TlaError) as e:
             G.run_gemm(case, W.gemm_inputs(case), sentinel=SENT[case.d_type], variant=variant)
         assert e.value.status == tla.ERR_UNSUPPORTED
@@ -325,9 +327,44 @@ def test_variant_info_reports_the_compiled_kernels():
     import tiled_layout_algebra_amd as tla
     for a_type in (W.BF16, W.F16, W.E4M3):
         infos = [tla.gemm_variant_info(v, a_type) for v in range(tla.GEMM_VARIANTS)]
-        assert [i["name"] for i in infos] == ["gemm_fast_256x256", "gemm_fast_128x128",
-                                              "gemm_general_128x128"]
+        assert [i["name"] for i in infos] == ["gemm_pingpong_256x256", "gemm_fast_128x128",
+                                              "gemm_general_128x128", "gemm_fast_256x256"]
+        assert infos[0]["threads"] == 512 and infos[0]["blocks_per_cu"] == 1
         for i in infos:
             assert i["threads"] in (256, 512) and i["lds_bytes"] > 0 and i["blocks_per_cu"] >= 1
             assert i["lds_bytes"] * i["blocks_per_cu"] <= 160 * 1024
         assert infos[0]["block_m"] == 256 and infos[2]["block_n"] == 128
+        assert infos[3]["block_m"] == 256
+
+
+# ------------------------------------------------- two-group 256x256 kernel
+
+@pytest.mark.parametrize("k_tiles", [1, 2, 3, 4])
+@pytest.mark.parametrize("a_type,d_type", [(W.BF16, W.BF16), (W.F16, W.F16), (W.E4M3, W.BF16)])
+def test_pingpong_few_k_tiles_bit_exact(k_tiles, a_type, d_type):
+    """The two-group kernel's prologue and last phases: 1 to 4 k-tiles of
+    128 bytes, ragged M and N (the last row block ends inside a 32-row copy
+    block), integer inputs (exact in fp32), forced variant 0."""
+    K = k_tiles * 128 // W.ITEMSIZE[a_type]
+    M, N = 300, 520
+    case = W.GemmCase(name="pp_k", M=M, N=N, K=K, a_type=a_type, b_type=a_type, d_type=d_type,
+                      alpha=1.5, beta=0.5, act=W.ACT_RELU, has_c=True, has_bias=True,
+                      seed=400 + k_tiles, dist_a="int3", dist_b="int3", dist_c="int3",
+                      dist_bias="eighths")
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT[d_type], variant=0)
+    assert G.padding_untouched(case, D, SENT[d_type])
+    want = W.encode(G.oracle_ref(case, inp), d_type).reshape(M, N)
+    assert np.array_equal(W.d_logical(case, D), want)
+
+
+def test_pingpong_e4m3_ragged_full():
+    """e4m3 on the two-group kernel with both extents ragged and a pitched D
+    (13 x 11 tiles of 256; rows and columns end mid-tile), every output
+    against the oracle within 5e-2 (1 + |ref|)."""
+    case = dataclasses.replace(W.GEMM_E4M3_8192, M=3100, N=2600, K=1024, lda=0, ldb=0, ldc=0,
+                               ldd=0)
+    case.__post_init__()
+    case.ldd += 24
+    assert G.variant(case) == "gemm_pingpong_256x256"
+    _check_full(case, W.gemm_inputs(case))

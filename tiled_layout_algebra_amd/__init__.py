@@ -197,7 +197,7 @@ def conv2d_fprop(x, w, y, N, H, W, C, K, R, S, dtype, stride=(1, 1), pad=(0, 0),
     _check(lib().tla_conv2d_fprop(ctypes.byref(a), _stream(stream, x, w, y)), "tla_conv2d_fprop")
 
 
-GEMM_VARIANTS = 3
+GEMM_VARIANTS = 4
 
 
 class GemmKernelInfo(ctypes.Structure):

@@ -1,9 +1,11 @@
 """Build libtla.so in-tree with hipcc for gfx950.
 
-    python -m tiled_layout_algebra_amd.build
+    python -m tiled_layout_algebra_amd.build [--changed]
 
 Every source under csrc/ is compiled to an object in _build/ (in parallel),
-then linked into tiled_layout_algebra_amd/libtla.so.  Always recompiles.
+then linked into tiled_layout_algebra_amd/libtla.so.  Recompiles everything
+unless --changed is given (then only sources newer than their object, or
+all of them when a header changed).
 """
 import os
 import subprocess
@@ -15,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtla.so")
-SOURCES = ["api.cpp", "algebra.cpp", "gemm.hip", "transpose.hip", "layout_eval.hip"]
+SOURCES = ["api.cpp", "algebra.cpp", "gemm.hip", "gemm_pingpong.hip", "transpose.hip",
+           "layout_eval.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -41,10 +44,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def _stale(src: str) -> bool:
+    """True if src's object is missing or older than src or any header."""
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [os.path.join(CSRC, src), os.path.join(ROOT, "include", "tla.h")]
+    for d, _, files in os.walk(CSRC):
+        deps += [os.path.join(d, f) for f in files if f.endswith((".hpp", ".h"))]
+    return any(os.path.getmtime(f) > t for f in deps)
+
+
+def build(verbose: bool = True, only_changed: bool = False) -> str:
+    """Compile every source (or, with only_changed, those whose object is
+    older than the source or any header) and link libtla.so."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    todo = [s for s in SOURCES if not only_changed or _stale(s)]
+    with ThreadPoolExecutor(max_workers=max(len(todo), 1)) as ex:
+        list(ex.map(_compile, todo))
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,4 +76,4 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(only_changed="--changed" in sys.argv[1:])

@@ -31,578 +31,10 @@
 //   general any order, pitch or alignment, ragged K: registers staged through
 //           a strip-mined thread map with per-element predicates; elements
 //           outside the matrix load as zero.
-#include <type_traits>
-
-#include "kernels.hpp"
-#include "tla/copy.hpp"
-#include "tla/layout.hpp"
-#include "tla/mfma.hpp"
+#include "gemm_common.hpp"
 
 namespace tla {
 namespace {
-
-constexpr int kThreads = 256;  // four wavefronts
-
-// LDS slab geometry for rows of kRowBytes bytes of K (a power of two between
-// 32 and 128): kChunks 16-byte chunks per row and the XOR swizzle
-// f(row) = (row / rows-per-256-bytes) mod kChunks, so the 16 rows a
-// quarter-wave reads at one logical chunk cover the 16 distinct 16-byte
-// bank groups of a 256-byte LDS window.
-template <int kRowBytes>
-struct Slab {
-  static constexpr int kChunks = kRowBytes / 16;
-  static constexpr int kRowShift = kRowBytes == 128 ? 1 : (kRowBytes == 64 ? 2 : 3);
-  using Swz = XorSwizzle<kChunks, kRowShift>;
-};
-
-// Workgroup barrier for LDS stages filled by direct copies.  __syncthreads()
-// would put a workgroup release fence in front of the barrier, and that fence
-// waits for every copy still in flight into LDS (vmcnt(0)) -- including the
-// ones issued for later stages, which would drain the pipeline at every
-// barrier.  Each wave instead waits for exactly the copies of the tile it
-// needs (wait_vmcnt) and then meets the others here; the acquire fence keeps
-// the LDS reads that follow from moving above the barrier.
-__device__ __forceinline__ void stage_barrier() {
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
-// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// p.flags: C / D / bias rows allow aligned 4-element (8-byte for 16-bit)
-// vectors; C / D rows (16-bit) allow aligned 16-byte vectors.
-enum : int { kCVec = 1, kDVec = 2, kBiasVec = 4, kC16 = 8, kD16 = 16 };
-
-struct GemmParams {
-  const uint8_t* A;
-  const uint8_t* B;
-  const uint8_t* C;
-  uint8_t* D;
-  const uint8_t* bias;
-  // (row, k) strides of the A view (rows = m) and the B view (rows = n), in
-  // elements; (m, n) strides of C and D.
-  int64_t a_sr, a_sk, b_sr, b_sk, c_sm, c_sn, d_sm, d_sn;
-  int M, N, K;
-  int c_type, d_type, bias_type, act;
-  float alpha, beta;
-  int tiles_m, tiles_n;
-  int flags;
-  // implicit-GEMM convolution view of A (used by the kConv kernels only):
-  // image H x W x C (NHWC), filter R x S, output P x Q, stride (u, v),
-  // padding (ph, pw), dilation (dh, dw)
-  int cH, cW, cC, cR, cS, cP, cQ, cu, cv, cph, cpw, cdh, cdw;
-};
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ lds_void_t* to_lds(void* p) { return (lds_void_t*)(p); }
-
-// ---------------------------------------------------------- tile scheduler
-// Workgroup b is dispatched to XCD b % 8.  Tile ids are handed out so that
-// each XCD gets a contiguous run of them, and runs are ordered GROUP_M tile
-// rows at a time (tile row fastest), so the workgroups sharing one XCD's L2
-// work on a compact block of D and reuse each other's A and B slabs.
-__device__ __forceinline__ void schedule(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int kXcds = 8, kGroupM = 4;
-  const int total = tiles_m * tiles_n;
-  int id = bid;
-  if (total % kXcds == 0) id = (bid % kXcds) * (total / kXcds) + bid / kXcds;
-  const int per_group = kGroupM * tiles_n;
-  const int first_m = (id / per_group) * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int in = id % per_group;
-  tm = first_m + in % gm;
-  tn = in / gm;
-}
-
-// ------------------------------------------------------------ fast loader
-// One k-tile slab of ROWS rows x kRowBytes bytes via direct global -> LDS
-// copies.  The strip-mined map (ROWS x kChunks chunks, 256 threads, one chunk
-// per access) puts thread t of iteration it at LDS slot t + 256*it, which is the
-// lane-linear slot the DMA writes; the lane fetches the logical chunk that
-// the swizzle assigns to that slot.
-template <int ROWS, int kRowBytes>
-__device__ __forceinline__ void dma_slab(const uint8_t* __restrict__ base, int64_t row_bytes,
-                                         int row0, int rows_valid, int64_t kbyte0, uint8_t* slab,
-                                         int tid) {
-  using Swz = typename Slab<kRowBytes>::Swz;
-  constexpr int kChunks = Slab<kRowBytes>::kChunks;
-  constexpr StripMinedMap map(ROWS, kChunks, kThreads, 1, ROWS * kChunks / kThreads);
-  static_assert(map.well_formed(), "slab thread map");
-#pragma unroll
-  for (int it = 0; it < map.I; ++it) {
-    const int r = map.strided(tid, it);
-    const int c = Swz::chunk(r, map.contiguous(tid, 0));
-    const int gr = min(row0 + r, rows_valid - 1);
-    const uint8_t* src = base + gr * row_bytes + kbyte0 + c * 16;
-    uint8_t* dst = slab + map.index(tid & ~63, it, 0) * 16;  // wave-uniform
-    __builtin_amdgcn_global_load_lds(src, to_lds(dst), 16, 0, 0);
-  }
-}
-
-// Instruction `it` of dma_slab on its own, so a kernel can spread the copy
-// of a slab between its matrix-core instructions.
-template <int ROWS, int kRowBytes, int NT = kThreads>
-__device__ __forceinline__ void dma_one(const uint8_t* __restrict__ base, int64_t row_bytes,
-                                        int row0, int rows_valid, int64_t kbyte0, uint8_t* slab,
-                                        int tid, int it) {
-  using Swz = typename Slab<kRowBytes>::Swz;
-  constexpr int kChunks = Slab<kRowBytes>::kChunks;
-  constexpr StripMinedMap map(ROWS, kChunks, NT, 1, ROWS * kChunks / NT);
-  const int r = map.strided(tid, it);
-  const int c = Swz::chunk(r, map.contiguous(tid, 0));
-  const int gr = min(row0 + r, rows_valid - 1);
-  const uint8_t* src = base + gr * row_bytes + kbyte0 + c * 16;
-  uint8_t* dst = slab + map.index(tid & ~63, it, 0) * 16;  // wave-uniform
-  __builtin_amdgcn_global_load_lds(src, to_lds(dst), 16, 0, 0);
-}
-
-// --------------------------------------------------------- general loader
-// Element-predicated, register-staged slab copy for any operand view
-// (row, k) -> row*s_r + k*s_k.  K-contiguous views use the row-contiguous
-// thread map (consecutive lanes walk K); the others use the column-major
-// variant (consecutive lanes walk rows, so each element load coalesces).
-template <int ROWS, int EB, int kRowBytes>
-struct RegSlab {
-  using Swz = typename Slab<kRowBytes>::Swz;
-  static constexpr int kChunks = Slab<kRowBytes>::kChunks;
-  static constexpr int kI = ROWS * kChunks / kThreads;
-  static constexpr int kCE = 16 / EB;  // elements per 16-byte chunk
-  i32x4 v[kI];
-
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t s_r, int64_t s_k,
-                                       int row0, int rows_valid, int k0, int K, bool vec_ok,
-                                       int tid) {
-    constexpr StripMinedMap kmap(ROWS, kChunks, kThreads, 1, kI, 1);
-    constexpr StripMinedMap rmap(ROWS, kChunks, kThreads, 1, kI, 0);
-    static_assert(kmap.well_formed() && rmap.well_formed(), "slab thread maps");
-    const bool kcontig = (s_k == 1);
-#pragma unroll
-    for (int it = 0; it < kI; ++it) {
-      const int r = kcontig ? kmap.row(tid, it, 0) : rmap.row(tid, it, 0);
-      const int c = kcontig ? kmap.col(tid, it, 0) : rmap.col(tid, it, 0);
-      const int gr = row0 + r;
-      const int gk = k0 + c * kCE;
-      i32x4 x = {0, 0, 0, 0};
-      if (gr < rows_valid) {
-        const uint8_t* p = base + (gr * s_r + (int64_t)gk * s_k) * EB;
-        if (vec_ok && kcontig && gk + kCE <= K) {
-          x = *(const i32x4*)p;
-        } else {
-          uint8_t bytes[16] = {};
-#pragma unroll
-          for (int e = 0; e < kCE; ++e) {
-            if (gk + e < K) {
-              const uint8_t* q = p + (int64_t)e * s_k * EB;
-#pragma unroll
-              for (int b = 0; b < EB; ++b) bytes[e * EB + b] = q[b];
-            }
-          }
-          x = __builtin_bit_cast(i32x4, bytes);
-        }
-      }
-      v[it] = x;
-    }
-  }
-
-  __device__ __forceinline__ void store(uint8_t* slab, bool kcontig, int tid) const {
-    constexpr StripMinedMap kmap(ROWS, kChunks, kThreads, 1, kI, 1);
-    constexpr StripMinedMap rmap(ROWS, kChunks, kThreads, 1, kI, 0);
-#pragma unroll
-    for (int it = 0; it < kI; ++it) {
-      const int r = kcontig ? kmap.row(tid, it, 0) : rmap.row(tid, it, 0);
-      const int c = kcontig ? kmap.col(tid, it, 0) : rmap.col(tid, it, 0);
-      *(i32x4*)(slab + r * kRowBytes + Swz::chunk(r, c) * 16) = v[it];
-    }
-  }
-};
-
-// ---------------------------------------------- implicit-GEMM A loader
-// The A operand of a convolution seen as a GEMM (the implicit GEMM of the
-// PitchLinearStripminedThreadMap walk-through, section 5.2): row m is the
-// output pixel (n, p, q) = (m / PQ, m / Q mod P, m mod Q), column k the
-// filter position and channel (r, s, c) = (k / (S C), k / C mod S, k mod C),
-// and the element is x[n, p u - ph + r dh, q v - pw + s dw, c] -- zero outside
-// the image.  The slab is walked with the same row-contiguous strip-mined
-// map as a K-contiguous operand; when C is a multiple of the vector width
-// (and the image is 16-byte aligned) a 16-byte chunk never straddles a
-// filter position, so one bounds check covers it.
-template <int ROWS, int EB, int kRowBytes>
-struct ConvSlab : RegSlab<ROWS, EB, kRowBytes> {
-  using Base = RegSlab<ROWS, EB, kRowBytes>;
-
-  __device__ __forceinline__ const uint8_t* at(const GemmParams& p, int n, int h0, int w0,
-                                               int k) const {
-    const int c = k % p.cC, rs = k / p.cC;
-    const int r = rs / p.cS, s = rs - r * p.cS;
-    const int h = h0 + r * p.cdh, w = w0 + s * p.cdw;
-    if (h < 0 || h >= p.cH || w < 0 || w >= p.cW) return nullptr;
-    return p.A + ((((int64_t)n * p.cH + h) * p.cW + w) * p.cC + c) * EB;
-  }
-
-  __device__ __forceinline__ void load_conv(const GemmParams& p, int row0, int k0, bool vec_ok,
-                                            int tid) {
-    constexpr StripMinedMap kmap(ROWS, Base::kChunks, kThreads, 1, Base::kI, 1);
-    constexpr int kCE = Base::kCE;
-    const int PQ = p.cP * p.cQ;
-#pragma unroll
-    for (int it = 0; it < Base::kI; ++it) {
-      const int m = row0 + kmap.row(tid, it, 0);
-      const int k = k0 + kmap.col(tid, it, 0) * kCE;
-      i32x4 x = {0, 0, 0, 0};
-      if (m < p.M) {
-        const int n = m / PQ, pq = m - n * PQ, pp = pq / p.cQ, qq = pq - pp * p.cQ;
-        const int h0 = pp * p.cu - p.cph, w0 = qq * p.cv - p.cpw;
-        if (vec_ok && k + kCE <= p.K) {
-          const uint8_t* src = at(p, n, h0, w0, k);
-          if (src) x = *(const i32x4*)src;
-        } else {
-          uint8_t bytes[16] = {};
-#pragma unroll
-          for (int e = 0; e < kCE; ++e) {
-            if (k + e < p.K) {
-              const uint8_t* src = at(p, n, h0, w0, k + e);
-              if (src) {
-#pragma unroll
-                for (int b = 0; b < EB; ++b) bytes[e * EB + b] = src[b];
-              }
-            }
-          }
-          x = __builtin_bit_cast(i32x4, bytes);
-        }
-      }
-      this->v[it] = x;
-    }
-  }
-};
-
-// ------------------------------------------------------- fragment loader
-// Lane l's operand fragment for MFMA k-step ks: row `row` of the slab, the
-// (l/32)-th kLaneBytes-wide half of the step's K bytes.
-template <int kCode, int kRowBytes>
-__device__ __forceinline__ typename MfmaAtom<kCode>::Frag load_frag(const uint8_t* slab, int row,
-                                                                   int ks, int lane) {
-  using Atom = MfmaAtom<kCode>;
-  using Swz = typename Slab<kRowBytes>::Swz;
-  constexpr int kStepBytes = Atom::kK * elem_bytes(kCode);
-  const int c0 = (ks * kStepBytes + (lane >> 5) * Atom::kLaneBytes) / 16;
-  const uint8_t* rowp = slab + row * kRowBytes;
-  if constexpr (Atom::kLaneBytes == 16) {
-    return *(const i32x4*)(rowp + Swz::chunk(row, c0) * 16);
-  } else {
-    i32x4 lo = *(const i32x4*)(rowp + Swz::chunk(row, c0) * 16);
-    i32x4 hi = *(const i32x4*)(rowp + Swz::chunk(row, c0 + 1) * 16);
-    return typename Atom::Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-}
-
-// ---------------------------------------------------------------- epilogue
-__device__ __forceinline__ float load_elem(const uint8_t* p, int type, int64_t idx) {
-  if (type == kF32) return ((const float*)p)[idx];
-  const uint16_t h = ((const uint16_t*)p)[idx];
-  if (type == kBF16) return __builtin_bit_cast(float, (uint32_t)h << 16);
-  return (float)__builtin_bit_cast(_Float16, h);
-}
-
-__device__ __forceinline__ uint16_t to_bits(float v, int type) {
-  if (type == kBF16) return __builtin_bit_cast(uint16_t, (__bf16)v);
-  return __builtin_bit_cast(uint16_t, (_Float16)v);
-}
-
-__device__ __forceinline__ void load4(const uint8_t* p, int type, int64_t idx, float (&x)[4]) {
-  if (type == kF32) {
-    const f32x4 v = *(const f32x4*)((const float*)p + idx);
-    x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
-  } else {
-    const uint2 u = *(const uint2*)((const uint16_t*)p + idx);
-    const uint32_t w[4] = {u.x & 0xFFFFu, u.x >> 16, u.y & 0xFFFFu, u.y >> 16};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      x[q] = (type == kBF16) ? __builtin_bit_cast(float, w[q] << 16)
-                             : (float)__builtin_bit_cast(_Float16, (uint16_t)w[q]);
-  }
-}
-
-__device__ __forceinline__ float activate(float y, int act) {
-  if (act == TLA_ACT_RELU) return y > 0.f ? y : 0.f;
-  if (act == TLA_ACT_GELU) return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f));
-  return y;
-}
-
-// Four consecutive columns n..n+3 of row m.
-__device__ __forceinline__ void epilogue4(const GemmParams& p, int m, int n, const float (&acc)[4]) {
-  if (m >= p.M || n >= p.N) return;
-  const bool full = n + 3 < p.N;
-  float y[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) y[q] = p.alpha * acc[q];
-  if (p.beta != 0.f) {
-    float c[4] = {0.f, 0.f, 0.f, 0.f};
-    if (full && (p.flags & kCVec)) {
-      load4(p.C, p.c_type, m * p.c_sm + (int64_t)n, c);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (n + q < p.N) c[q] = load_elem(p.C, p.c_type, m * p.c_sm + (int64_t)(n + q) * p.c_sn);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) y[q] += p.beta * c[q];
-  }
-  if (p.bias) {
-    float b[4] = {0.f, 0.f, 0.f, 0.f};
-    if (full && (p.flags & kBiasVec)) {
-      load4(p.bias, p.bias_type, n, b);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (n + q < p.N) b[q] = load_elem(p.bias, p.bias_type, n + q);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) y[q] += b[q];
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) y[q] = activate(y[q], p.act);
-  uint16_t* D = (uint16_t*)p.D;
-  if (full && (p.flags & kDVec)) {
-    uint2 u;
-    u.x = (uint32_t)to_bits(y[0], p.d_type) | ((uint32_t)to_bits(y[1], p.d_type) << 16);
-    u.y = (uint32_t)to_bits(y[2], p.d_type) | ((uint32_t)to_bits(y[3], p.d_type) << 16);
-    *(uint2*)(D + m * p.d_sm + n) = u;
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (n + q < p.N) D[m * p.d_sm + (int64_t)(n + q) * p.d_sn] = to_bits(y[q], p.d_type);
-  }
-}
-
-// ------------------------------------------- specialised full-tile epilogue
-// The two fast epilogue paths below are compiled once per activation and
-// per D type, so the per-element work is straight-line code; C and bias
-// (bf16 or fp16) are widened with a select rather than a branch.
-__device__ __forceinline__ float widen16(uint32_t w, bool bf16) {
-  const float b = __builtin_bit_cast(float, w << 16);
-  const float h = (float)__builtin_bit_cast(_Float16, (uint16_t)w);
-  return bf16 ? b : h;
-}
-
-template <int kAct>
-__device__ __forceinline__ float act_t(float y) {
-  if constexpr (kAct == TLA_ACT_RELU) return y > 0.f ? y : 0.f;
-  if constexpr (kAct == TLA_ACT_GELU) return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f));
-  return y;
-}
-
-template <bool kBf16>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  if constexpr (kBf16)
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
-  else
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
-}
-
-// y = act(alpha*acc + beta*c + bias) for the four values of group g of tile
-// (i, j); c and bias arrive as packed 16-bit pairs.
-template <int kAct, bool kDBf16>
-__device__ __forceinline__ uint2 epi_group(const f32x16& acc, int g, uint2 c, uint2 b, float alpha,
-                                           float beta, bool c_bf16, bool b_bf16) {
-  const uint32_t cw[4] = {c.x, c.x >> 16, c.y, c.y >> 16};
-  const uint32_t bw[4] = {b.x, b.x >> 16, b.y, b.y >> 16};
-  float y[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float v = alpha * acc[4 * g + q];
-    v += beta * widen16(cw[q] & 0xFFFFu, c_bf16);
-    y[q] = act_t<kAct>(v + widen16(bw[q] & 0xFFFFu, b_bf16));
-  }
-  return uint2{pack2<kDBf16>(y[0], y[1]), pack2<kDBf16>(y[2], y[3])};
-}
-
-// This lane's 16-bit bias values for its column groups, all loads issued
-// before any is used (zero bits when there is no bias).
-template <int FN>
-__device__ __forceinline__ void load_bias16(const GemmParams& p, int n_base, int half,
-                                            uint2 (&braw)[FN][4]) {
-  static_for<FN>([&](auto j) { static_for<4>([&](auto g) { braw[j][g] = uint2{0u, 0u}; }); });
-  if (p.bias) {
-    const uint2* b = (const uint2*)((const uint16_t*)p.bias + n_base + 4 * half);
-    static_for<FN>([&](auto j) { static_for<4>([&](auto g) { braw[j][g] = b[8 * j + 2 * g]; }); });
-  }
-}
-
-// Full wave tile through LDS.  In the MFMA result layout a lane holds four
-// consecutive columns of one row, so a direct global access touches 32 rows
-// 16 bytes at a time.  Instead the wave copies its C sub-tile (WM rows of
-// 64*FN bytes) into its own LDS region with whole-row direct copies, applies
-// the epilogue reading C there in the MFMA layout, writes the 16-bit result
-// back in place and stores D from LDS as whole rows.  The region's 16-byte
-// chunks are XOR-swizzled by row so that the lane-per-row accesses of one
-// instruction fall into distinct LDS banks.
-template <int kAct, bool kDBf16, int FM, int FN>
-__device__ __forceinline__ void epilogue_lds(const GemmParams& p, int m_base, int n_base, int lane,
-                                             const f32x16 (&acc)[FM][FN], uint8_t* region) {
-  constexpr int kRowB = 64 * FN, kCh = kRowB / 16, kRowsPerKiB = 1024 / kRowB;
-  static_assert(kCh == 4 || kCh == 8 || kCh == 16, "row width");
-  constexpr int kIters = 32 * FM * kRowB / 1024;
-  auto swz = [](int r, int c) { return c ^ ((r / (16 / kCh)) & (kCh - 1)); };
-  const int row = lane & 31, half = lane >> 5;
-  const int rr = lane / kCh, cs = lane % kCh;  // row-wise view of one KiB
-  const bool has_c = p.beta != 0.f;
-  if (has_c) {
-    const uint8_t* C = p.C + ((int64_t)m_base * p.c_sm + n_base) * 2;
-    static_for<kIters>([&](auto t) {
-      const int r = kRowsPerKiB * t + rr;
-      const uint8_t* src = C + (int64_t)r * p.c_sm * 2 + swz(r, cs) * 16;
-      __builtin_amdgcn_global_load_lds(src, to_lds(region + t * 1024), 16, 0, 0);
-    });
-  }
-  uint2 braw[FN][4];
-  load_bias16<FN>(p, n_base, half, braw);
-  wait_vmcnt<0>();  // this wave's C copies have landed in its region
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const bool c_bf16 = p.c_type == kBF16, b_bf16 = p.bias_type == kBF16;
-  const float beta = has_c ? p.beta : 0.f;
-  static_for<FM>([&](auto i) {
-    static_for<FN>([&](auto j) {
-      static_for<4>([&](auto g) {
-        const int r = 32 * i + row;
-        uint8_t* slot = region + r * kRowB + swz(r, 4 * j + g) * 16 + 8 * half;
-        const uint2 c = has_c ? *(const uint2*)slot : uint2{0u, 0u};
-        *(uint2*)slot = epi_group<kAct, kDBf16>(acc[i][j], g, c, braw[j][g], p.alpha, beta, c_bf16, b_bf16);
-      });
-    });
-  });
-  uint8_t* D = p.D + ((int64_t)m_base * p.d_sm + n_base) * 2;
-  static_for<kIters>([&](auto t) {
-    const int r = kRowsPerKiB * t + rr;
-    const i32x4 v = *(const i32x4*)(region + t * 1024 + lane * 16);
-    *(i32x4*)(D + (int64_t)r * p.d_sm * 2 + swz(r, cs) * 16) = v;
-  });
-}
-
-// Full wave tile straight from and to global memory with 8-byte vectors;
-// all C and bias loads are issued before the arithmetic.
-template <int kAct, bool kDBf16, int FM, int FN>
-__device__ __forceinline__ void epilogue_direct(const GemmParams& p, int m_base, int n_base, int lane,
-                                                const f32x16 (&acc)[FM][FN]) {
-  const int row = lane & 31, half = lane >> 5;
-  const bool has_c = p.beta != 0.f;
-  uint2 c[FM][FN][4];
-  if (has_c) {
-    const uint16_t* C = (const uint16_t*)p.C;
-    static_for<FM>([&](auto i) {
-      static_for<FN>([&](auto j) {
-        static_for<4>([&](auto g) {
-          c[i][j][g] = *(const uint2*)(C + (int64_t)(m_base + 32 * i + row) * p.c_sm + n_base + 32 * j +
-                                       8 * g + 4 * half);
-        });
-      });
-    });
-  } else {
-    static_for<FM>([&](auto i) {
-      static_for<FN>([&](auto j) { static_for<4>([&](auto g) { c[i][j][g] = uint2{0u, 0u}; }); });
-    });
-  }
-  uint2 braw[FN][4];
-  load_bias16<FN>(p, n_base, half, braw);
-  const bool c_bf16 = p.c_type == kBF16, b_bf16 = p.bias_type == kBF16;
-  const float beta = has_c ? p.beta : 0.f;
-  uint16_t* D = (uint16_t*)p.D;
-  static_for<FM>([&](auto i) {
-    static_for<FN>([&](auto j) {
-      static_for<4>([&](auto g) {
-        *(uint2*)(D + (int64_t)(m_base + 32 * i + row) * p.d_sm + n_base + 32 * j + 8 * g + 4 * half) =
-            epi_group<kAct, kDBf16>(acc[i][j], g, c[i][j][g], braw[j][g], p.alpha, beta, c_bf16, b_bf16);
-      });
-    });
-  });
-}
-
-template <bool kLds, int kAct, bool kDBf16, int FM, int FN>
-__device__ __forceinline__ void epilogue_fast(const GemmParams& p, int m_base, int n_base, int lane,
-                                              const f32x16 (&acc)[FM][FN], uint8_t* region) {
-  if constexpr (kLds)
-    epilogue_lds<kAct, kDBf16, FM, FN>(p, m_base, n_base, lane, acc, region);
-  else
-    epilogue_direct<kAct, kDBf16, FM, FN>(p, m_base, n_base, lane, acc);
-}
-
-template <bool kLds, int FM, int FN>
-__device__ __forceinline__ void epilogue_switch(const GemmParams& p, int m_base, int n_base, int lane,
-                                                const f32x16 (&acc)[FM][FN], uint8_t* region) {
-  const bool dbf = p.d_type == kBF16;
-  switch (p.act) {
-    case TLA_ACT_RELU:
-      if (dbf) epilogue_fast<kLds, TLA_ACT_RELU, true>(p, m_base, n_base, lane, acc, region);
-      else epilogue_fast<kLds, TLA_ACT_RELU, false>(p, m_base, n_base, lane, acc, region);
-      break;
-    case TLA_ACT_GELU:
-      if (dbf) epilogue_fast<kLds, TLA_ACT_GELU, true>(p, m_base, n_base, lane, acc, region);
-      else epilogue_fast<kLds, TLA_ACT_GELU, false>(p, m_base, n_base, lane, acc, region);
-      break;
-    default:
-      if (dbf) epilogue_fast<kLds, TLA_ACT_NONE, true>(p, m_base, n_base, lane, acc, region);
-      else epilogue_fast<kLds, TLA_ACT_NONE, false>(p, m_base, n_base, lane, acc, region);
-      break;
-  }
-}
-
-// The epilogue of one wavefront's FM x FN grid of 32x32 accumulator tiles,
-// rows m_base + 32i + lane%32, column groups n_base + 32j + 8g + 4(lane/32).
-// `region` is this wave's 32*FM x 64*FN-byte piece of LDS, free for reuse
-// (the caller has synchronised the workgroup after its last LDS read), or
-// null.  A wave tile inside D with 16-bit C (or no C) and bias takes the LDS
-// path when C and D rows allow 16-byte vectors, else the direct path with
-// 8-byte vectors; anything else (edge tiles, fp32 C or bias, strided C or D)
-// goes group by group through the predicated epilogue4.
-template <int FM, int FN>
-__device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, int n_base, int lane,
-                                               const f32x16 (&acc)[FM][FN], uint8_t* region) {
-  const bool full = m_base + 32 * FM <= p.M && n_base + 32 * FN <= p.N;
-  const bool b_ok = !p.bias || ((p.flags & kBiasVec) && p.bias_type != kF32);
-  const bool c16 = p.c_type != kF32;
-  if (full && b_ok && region && (p.flags & kD16) && (p.beta == 0.f || (c16 && (p.flags & kC16)))) {
-    epilogue_switch<true, FM, FN>(p, m_base, n_base, lane, acc, region);
-  } else if (full && b_ok && (p.flags & kDVec) && (p.beta == 0.f || (c16 && (p.flags & kCVec)))) {
-    epilogue_switch<false, FM, FN>(p, m_base, n_base, lane, acc, region);
-  } else {
-    static_for<FM>([&](auto i) {
-      const int m = m_base + 32 * i + mfma32_acc_col(lane, 0);
-      static_for<FN>([&](auto j) {
-        static_for<4>([&](auto g) {
-          const int n = n_base + 32 * j + mfma32_acc_row(lane, 4 * g);
-          const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                              acc[i][j][4 * g + 3]};
-          epilogue4(p, m, n, v);
-        });
-      });
-    });
-  }
-}
-
-// ------------------------------------------------------------- fast kernel
-// 16 bytes per lane from base + voffset + soffset into LDS, landing
-// lane-linearly from the wave-uniform address `lds`: a raw buffer load whose
-// per-lane 32-bit offset and uniform offset stay separate registers, so the
-// loop spends no vector instructions on copy addresses.  Every offset the
-// kernel forms is below 2^31 (checked by the host).
-// `records` bounds the buffer: a lane whose offset lies past it reads zeros
-// (the raw buffer range check) and touches no memory.
-__device__ __forceinline__ void dma16_buf(const uint8_t* base, uint32_t voffset, uint32_t soffset,
-                                          uint8_t* lds, int records = 0x7FFFFFFF) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, records, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset,
-                                           soffset, 0, 0);
-#endif
-}
 
 // Both operands K-contiguous with 16-byte aligned rows, K a multiple of the
 // slab width.  LDS holds kStages A slabs, then kStages B slabs; k-tile kt
@@ -988,14 +420,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 }
 
 // ----------------------------------------------------------------- dispatch
-bool aligned(const void* p, int64_t bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
-
-void set_grid(GemmParams& p, int BM, int BN, int64_t* grid) {
-  p.tiles_m = (p.M + BM - 1) / BM;
-  p.tiles_n = (p.N + BN - 1) / BN;
-  *grid = (int64_t)p.tiles_m * p.tiles_n;
-}
-
 template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront, int kWM, int kWN,
           bool kConv = false>
 int launch_fast(const GemmParams& p0, hipStream_t stream) {
@@ -1024,35 +448,35 @@ int launch_two_stage(const GemmParams& p0, hipStream_t stream) {
 // The variants the library ships.  Every fast variant moves whole 128-byte
 // K rows per copy (the direct-to-LDS copy rate per compute unit halves with
 // every halving of the row width), so K must be a multiple of 128 bytes.
-//   16-bit, >= 128 tiles of 256x256: 8 wavefronts (2x4, 128x64 each), two
-//     stages, each tile's copies issued during the first MFMA step of the
-//     tile before (measured ~1 % ahead of spreading them over two or all
-//     four steps).
-//   16-bit, smaller: 128x128, 4 wavefronts, three stages.
-//   e4m3: the two-stage kernel (its 32-byte fragments do not fit the
-//     8-wavefront register budget).
+//   0 two-group 256x256 kernel (gemm_pingpong.hip), any operand type: two
+//     groups of four wavefronts (2x2 waves of 64x128 each) alternate
+//     between MFMA-only and memory phases.
+//   1 128x128 tiles.  16-bit: 8 wavefronts (2x4 of 64x32), three stages;
+//     e4m3: the 4-wavefront (2x2 of 64x64) two-stage kernel.
+//   2 the register-staged general kernel, 128x128, 4 wavefronts (2x2).
+//   3 the single-group 256x256 kernel.  16-bit: 8 wavefronts (2x4 of
+//     128x64), two stages, each tile's copies issued between the MFMAs of
+//     the first k-step of the tile before; e4m3: 4 wavefronts (2x2 of
+//     128x128), two stages.
 int fast_slab_bytes(int) { return 128; }
 
-const char* const kVariantNames[kGemmVariants] = {"gemm_fast_256x256", "gemm_fast_128x128",
-                                                  "gemm_general_128x128"};
-const int kVariantTile[kGemmVariants] = {256, 128, 128};
+const char* const kVariantNames[kGemmVariants] = {"gemm_pingpong_256x256", "gemm_fast_128x128",
+                                                  "gemm_general_128x128", "gemm_fast_256x256"};
+const int kVariantTile[kGemmVariants] = {256, 128, 128, 256};
 
 template <int kCode>
 int dispatch_typed(const GemmParams& p, bool fast, bool big, hipStream_t s, bool dry,
                    const char** name, int forced) {
-  // e4m3: the 128x128 kernel (two workgroups per compute unit) measured
-  // ahead of 256x256 at every size of the variant sweep (8192^3: 644 vs
-  // 725 us), so it is the automatic choice whenever the fast layout holds.
-  const bool use_big = big && kCode != kE4M3;
-  const int v = forced >= 0 ? forced : (fast ? (use_big ? 0 : 1) : 2);
-  if (v < 2 && !fast) return TLA_ERR_UNSUPPORTED;  // a fast variant needs the fast layout
+  const int v = forced >= 0 ? forced : (fast ? (big ? 0 : 1) : 2);
+  if (v != 2 && !fast) return TLA_ERR_UNSUPPORTED;  // a fast variant needs the fast layout
   if (name) *name = kVariantNames[v];
   if (dry) return TLA_OK;
+  if (v == 0) return launch_pingpong(p, kCode, s);
   if constexpr (kCode == kE4M3) {
-    if (v == 0) return launch_two_stage<kCode, 256, 256, 128, true>(p, s);
+    if (v == 3) return launch_two_stage<kCode, 256, 256, 128, true>(p, s);
     if (v == 1) return launch_two_stage<kCode, 128, 128, 128, true>(p, s);
   } else {
-    if (v == 0) return launch_fast<kCode, 256, 256, 128, 2, 1, 2, 4>(p, s);
+    if (v == 3) return launch_fast<kCode, 256, 256, 128, 2, 1, 2, 4>(p, s);
     // 8 wavefronts of 64 x 32 (two per SIMD): 9.2 us at 1024^3 and 20.3 us
     // at 2048^3, against 11.1 and 21.7 us for 4 wavefronts of 64 x 64
     if (v == 1) return launch_fast<kCode, 128, 128, 128, 3, 1, 2, 4>(p, s);
@@ -1064,11 +488,15 @@ int dispatch_typed(const GemmParams& p, bool fast, bool big, hipStream_t s, bool
 template <int kCode>
 const void* variant_kernel(int v, int* threads) {
   *threads = kThreads;
+  if (v == 0) {
+    *threads = 512;
+    return pingpong_kernel(kCode);
+  }
   if constexpr (kCode == kE4M3) {
-    if (v == 0) return (const void*)gemm_kernel<kCode, 256, 256, 128, 2, true>;
+    if (v == 3) return (const void*)gemm_kernel<kCode, 256, 256, 128, 2, true>;
     if (v == 1) return (const void*)gemm_kernel<kCode, 128, 128, 128, 2, true>;
   } else {
-    if (v == 0) {
+    if (v == 3) {
       *threads = 512;
       return (const void*)gemm_fast_kernel<kCode, 256, 256, 128, 2, 1, 2, 4>;
     }

@@ -38,8 +38,9 @@ struct ConvProblem {
 };
 int conv_dispatch(const ConvProblem& c, hipStream_t stream);
 
-// GEMM kernel variants: 0 fast 256x256, 1 fast 128x128, 2 general 128x128.
-constexpr int kGemmVariants = 3;
+// GEMM kernel variants: 0 two-group 256x256, 1 fast 128x128, 2 general
+// 128x128, 3 single-group 256x256.
+constexpr int kGemmVariants = 4;
 struct GemmKernelInfo {
   const char* name;
   int tile, threads, lds_bytes, vgprs, blocks_per_cu;
