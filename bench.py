@@ -11,7 +11,9 @@ per launch over its average launch time, measured with HIP events recorded
 on the launch stream); the transpose's GB/s (algorithmic bytes: one read and
 one write of the matrix) is reported beside it, each with its roofline.
 After the step loop the e4m3 8192^3 + GELU GEMM ("fp8", against the fp8
-peak) and the fp16 256^3 GEMM ("f16_256") are timed on their own.
+peak), the fp16 256^3 GEMM ("f16_256") and a row-major to row-major copy of
+the transpose's matrix (transpose.copy_ceiling: the same bytes with
+unit-stride runs on both sides) are timed on their own.
 `cpu_baseline` times the oracle on a bounded row sample of the bf16 GEMM
 (and of the fp8 GEMM and the transpose, inside their entries).
 
@@ -48,9 +50,6 @@ def parse():
                     help="skip the separately timed fp8 8192^3 and fp16 256^3 GEMMs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="append a plain 1 GiB device-to-device copy to every step (a kernel "
-                         "of known traffic, for scaling HBM byte counters)")
     ap.add_argument("--variants", action="store_true",
                     help="instead of the JSON line: run the bf16 4096^3 and e4m3 8192^3 "
                          "workloads with every fast GEMM variant forced (a short program "
@@ -172,35 +171,40 @@ def source_sha(kernel_files):
     return h.hexdigest()[:16]
 
 
-def hbm_traffic(prefix, kernel_file):
-    """HBM bytes per launch recorded in profiles/hbm_traffic.txt for the kernel
-    whose label starts with `prefix`, if its sources are unchanged since the
-    counters were taken; else None."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+def kernel_counters(label, kernel_files):
+    """Counter results recorded in profiles/kernel_counters.txt for the kernel
+    `label`, if its sources are unchanged since the counters were taken:
+    dict(clock_ghz, mfma_busy, lds_conflict_rate, traffic); else None."""
+    path = os.path.join(ROOT, "profiles", "kernel_counters.txt")
     if not os.path.exists(path):
         return None
-    sha = source_sha(kernel_file)
-    with open(path) as fh:
-        for line in fh:
-            parts = line.split()
-            if len(parts) == 5 and not line.startswith("#") and parts[0].startswith(prefix) \
-                    and parts[1] == sha:
-                return int(parts[4])
-    return None
-
-
-def engine_clock(prefix, kernel_file):
-    """The engine clock (GHz) measured during `prefix`'s kernel, from
-    profiles/engine_clock.txt, or None when the kernel changed since."""
-    path = os.path.join(ROOT, "profiles", "engine_clock.txt")
-    if not os.path.exists(path):
-        return None
-    sha = source_sha(kernel_file)
+    sha = source_sha(kernel_files)
     for line in open(path):
         f = line.split()
-        if len(f) == 4 and f[0].startswith(prefix) and f[1] == sha:
-            return float(f[2])
+        if len(f) == 7 and not line.startswith("#") and f[0] == label and f[1] == sha:
+            conf = float(f[4])
+            return {"clock_ghz": float(f[2]), "mfma_busy": float(f[3]),
+                    "lds_conflict_rate": None if conf != conf else conf,
+                    "traffic": int(f[5]) + int(f[6])}
     return None
+
+
+def roofline(achieved, peak, bound, unit, t, counters):
+    """The roofline object of one kernel: achieved vs the nameplate peak, the
+    launch times, and the counter results when they match the sources."""
+    r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": counters["traffic"] if counters else None,
+         "kernel_us": round(t.mean() * 1e6, 2), "kernel_us_min": round(t.min() * 1e6, 2)}
+    if counters:
+        clk = counters["clock_ghz"]
+        # the engine clock the counters saw during this kernel, and the
+        # fraction of the peak at that clock (nameplate: 2.4 GHz)
+        r["clock_ghz"] = clk
+        r["frac_at_clock"] = round(achieved / (peak * clk / 2.4), 4)
+        if bound == "mfma":
+            r["mfma_busy"] = counters["mfma_busy"]
+            r["lds_conflict_rate"] = counters["lds_conflict_rate"]
+    return r
 
 
 def cpu_baseline(case, inp, target_s):
@@ -290,6 +294,7 @@ def extra_gemm(tla, W, case, peak, stream, warmup, steps, cpu_s):
     run = gemm_call(tla, case, dA, dB, dD, dC, dbias, stream)
     t = time_launches(run, stream, warmup, steps)
     tf = case.flops() / t.mean() / 1e12
+    label = {W.E4M3: "gemm_pingpong_kernel<e4m3>"}.get(case.a_type)
     out = {"workload": case.name, "variant": tla.gemm_variant(
                case.M, case.N, case.K, dA, case.a_type, case.a_order, case.lda, dB, case.b_type,
                case.b_order, case.ldb, dD, case.d_type, case.d_order, case.ldd, C=dC,
@@ -297,10 +302,8 @@ def extra_gemm(tla, W, case, peak, stream, warmup, steps, cpu_s):
                alpha=case.alpha, beta=case.beta, scale_a=case.scale_a, scale_b=case.scale_b,
                act=case.act),
            "value": round(tf, 2), "unit": "TFLOP/s",
-           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
-                        "unit": "TFLOP/s", "frac": round(tf / peak, 4),
-                        "kernel_us": round(t.mean() * 1e6, 2),
-                        "kernel_us_min": round(t.min() * 1e6, 2)}}
+           "roofline": roofline(tf, peak, "mfma", "TFLOP/s", t,
+                                kernel_counters(label, GEMM_SOURCES) if label else None)}
     if cpu_s > 0:
         out["cpu_baseline"] = cpu_baseline(case, inp, cpu_s)
     del dA, dB, dC, dbias, dD
@@ -402,15 +405,8 @@ def main():
         tla.thread_map_eval(tmc.R, tmc.C, tmc.T, tmc.V, tmc.I, tmc.contiguous_dim, tmc.R - 1,
                             tmc.C, midx, mval, stream=stream.cuda_stream)
 
-    if args.calibrate_copy:
-        csrc = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
-        cdst = torch.empty_like(csrc)
-        csrc.fill_(1)
-
     def step():
         gemm(); transpose(); tmap()
-        if args.calibrate_copy:
-            cdst.copy_(csrc)
 
     for _ in range(args.warmup):
         step()
@@ -428,8 +424,6 @@ def main():
         ev[s][2].record(stream)
         tmap()
         ev[s][3].record(stream)
-        if args.calibrate_copy:
-            cdst.copy_(csrc)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -438,7 +432,6 @@ def main():
     gemm_tflops = g.flops() / t_gemm.mean() / 1e12
     tr_gbs = tc.bytes_moved() / t_tr.mean() / 1e9
 
-    clk = engine_clock("gemm", GEMM_SOURCES)
     out = {
         "metric": METRIC,
         "value": round(gemm_tflops, 2),
@@ -458,24 +451,28 @@ def main():
                             "alpha": g.alpha, "beta": g.beta, "act": "relu", "seed": g.seed,
                             "variant": variant},
                    "transpose": {"M": tc.M, "N": tc.N, "elem_bytes": 4, "seed": tc.seed}},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": hbm_traffic("gemm", GEMM_SOURCES),
-                     "kernel_us": round(t_gemm.mean() * 1e6, 2),
-                     "kernel_us_min": round(t_gemm.min() * 1e6, 2),
-                     # the engine clock the counters saw during this kernel, and the
-                     # fraction of the MFMA peak at that clock (nameplate: 2.4 GHz)
-                     "clock_ghz": clk,
-                     "frac_at_clock": (round(gemm_tflops / (PEAK_BF16_TFLOPS * clk / 2.4), 4)
-                                       if clk else None)},
+        "roofline": roofline(gemm_tflops, PEAK_BF16_TFLOPS, "mfma", "TFLOP/s", t_gemm,
+                             kernel_counters("gemm_pingpong_kernel<bf16>", GEMM_SOURCES)),
         "transpose": {"value": round(tr_gbs, 1), "unit": "GB/s",
-                      "roofline": {"bound": "hbm", "achieved": round(tr_gbs, 1),
-                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                   "frac": round(tr_gbs / PEAK_HBM_GBS, 4),
-                                   "traffic": hbm_traffic("transpose", TRANSPOSE_SOURCES),
-                                   "kernel_us": round(t_tr.mean() * 1e6, 2),
-                                   "kernel_us_min": round(t_tr.min() * 1e6, 2)}},
+                      "roofline": roofline(tr_gbs, PEAK_HBM_GBS, "hbm", "GB/s", t_tr,
+                                           kernel_counters("transpose4_kernel<1,4>",
+                                                           TRANSPOSE_SOURCES))},
     }
+    # The identity-layout copy of the same matrix (same bytes, unit-stride
+    # runs on both sides), timed on its own: the memory-system ceiling the
+    # transpose is measured against.
+    cdst = torch.empty_like(tsrc)
+
+    def copy():
+        tla.tiled_copy(tsrc, tc.N, cdst, tc.N, tc.M, tc.N, 4, stream=stream.cuda_stream)
+    t_cp = time_launches(copy, stream, max(args.warmup // 20, 3), K)
+    cp_gbs = tc.bytes_moved() / t_cp.mean() / 1e9
+    out["transpose"]["copy_ceiling"] = {
+        "value": round(cp_gbs, 1), "unit": "GB/s", "frac_of_peak": round(cp_gbs / PEAK_HBM_GBS, 4),
+        "kernel_us": round(t_cp.mean() * 1e6, 2),
+        "transpose_frac_of_copy": round(tr_gbs / cp_gbs, 4)}
+    del cdst
+
     # The other two measured GEMMs, each timed on its own after the step loop
     # (not part of a step): the fp8 8192^3 + GELU against the fp8 peak, and
     # the launch-bound fp16 256^3.

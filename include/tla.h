@@ -169,6 +169,21 @@ int tla_gemm_variant_info(int32_t variant, int32_t a_type, tla_gemm_kernel_info 
 int tla_tiled_transpose(const void *src, int64_t ld_src, void *dst, int64_t ld_dst,
                         int64_t M, int64_t N, int32_t elem_bytes, void *stream);
 
+/*
+ * The identity-layout case of the same layout-driven copy: a row-major
+ * M x N source to a row-major destination, bit for bit,
+ *     dst[m*ld_dst + n] = src[m*ld_src + n]      (element units)
+ * ("什么是 CuTe ?": a copy between two layouts over one shape; here both
+ * are row-major).  It moves the same bytes as tla_tiled_transpose with
+ * unit-stride runs on both sides, so it gives the memory-system ceiling a
+ * transpose is measured against.  elem_bytes: 1, 2, 4, 8 or 16; ld_src >= N,
+ * ld_dst >= N; element-aligned pointers (TLA_ERR_INVALID_ARG otherwise);
+ * non-overlapping byte ranges (TLA_ERR_OVERLAP).  M == 0 or N == 0 is a
+ * no-op; destination padding is never written.
+ */
+int tla_tiled_copy(const void *src, int64_t ld_src, void *dst, int64_t ld_dst,
+                   int64_t M, int64_t N, int32_t elem_bytes, void *stream);
+
 /* ------------------------------------------------------ convolution */
 /*
  * Forward convolution as an implicit GEMM (PitchLinearStripminedThreadMap

@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_gemm_points.restype = I32
         L.oracle_transpose.argtypes = [P, I64, P, I64, I64, I64, I32]
         L.oracle_transpose.restype = I32
+        L.oracle_copy2d.argtypes = [P, I64, P, I64, I64, I64, I32]
+        L.oracle_copy2d.restype = I32
         L.oracle_conv2d.argtypes = [ctypes.POINTER(ConvArgs), P, I32]
         L.oracle_conv2d.restype = I32
         L.oracle_conv2d_points.argtypes = [ctypes.POINTER(ConvArgs), P, P, I64, P, I32]

@@ -1,5 +1,6 @@
 """ctypes front-end of the C oracle (``oracle.c``): decoders, binary64 GEMM
-with the scalar epilogue, sampled GEMM outputs, bit-copy transpose.
+with the scalar epilogue, sampled GEMM outputs, bit-copy transpose and
+pitched 2-D copy.
 
 Test infrastructure only (see the package docstring).  Operands are host
 numpy arrays holding the raw storage bits (uint16 for fp16/bf16, uint8 for
@@ -111,6 +112,19 @@ def transpose(src: np.ndarray, M: int, N: int, ld_src: int, ld_dst: int,
     rc = lib().oracle_transpose(_ptr(src), ld_src, _ptr(dst), ld_dst, M, N, eb)
     if rc:
         raise ValueError("oracle_transpose failed (%d)" % rc)
+    return dst
+
+
+def copy2d(src: np.ndarray, M: int, N: int, ld_src: int, ld_dst: int,
+           dst: np.ndarray = None) -> np.ndarray:
+    """dst[m*ld_dst + n] = src[m*ld_src + n], raw bits (any itemsize)."""
+    src = np.ascontiguousarray(src).reshape(-1)
+    eb = src.dtype.itemsize
+    if dst is None:
+        dst = np.zeros(max(ld_dst * M, 0), dtype=src.dtype)
+    rc = lib().oracle_copy2d(_ptr(src), ld_src, _ptr(dst), ld_dst, M, N, eb)
+    if rc:
+        raise ValueError("oracle_copy2d failed (%d)" % rc)
     return dst
 
 

@@ -311,6 +311,23 @@ int oracle_transpose(const void *src, int64_t ld_src, void *dst, int64_t ld_dst,
   return 0;
 }
 
+/* Row-major S (M x N, pitch ld_src) -> row-major D (pitch ld_dst): the
+ * identity case of the same layout-driven copy, D(m,n) = S(m,n) bit for
+ * bit, i.e. dst[m*ld_dst + n] = src[m*ld_src + n].  Padding of D is not
+ * written. */
+int oracle_copy2d(const void *src, int64_t ld_src, void *dst, int64_t ld_dst,
+                  int64_t M, int64_t N, int32_t eb) {
+  if (M < 0 || N < 0 || eb <= 0) return -1;
+  if (M == 0 || N == 0) return 0;
+  if (!src || !dst || ld_src < N || ld_dst < N) return -1;
+  const char *s = (const char *)src;
+  char *d = (char *)dst;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n)
+      memcpy(d + (m * ld_dst + n) * eb, s + (m * ld_src + n) * eb, (size_t)eb);
+  return 0;
+}
+
 /* ----------------------------------------------------------- convolution */
 
 /* Forward convolution (cross-correlation) as the implicit GEMM of the

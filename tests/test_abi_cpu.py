@@ -119,6 +119,18 @@ def test_transpose_argument_errors():
     assert f(FAKE + 64, 8, FAKE, 8, 8, 8, 4, None) == tla.ERR_OVERLAP
 
 
+def test_copy_argument_errors():
+    f = tla.lib().tla_tiled_copy
+    assert f(FAKE, 8, FAKE * 4, 8, -1, 8, 4, None) == tla.ERR_INVALID_ARG
+    assert f(FAKE, 8, FAKE * 4, 8, 8, 8, 3, None) == tla.ERR_UNSUPPORTED
+    assert f(FAKE, 8, FAKE * 4, 8, 0, 8, 4, None) == tla.OK          # empty
+    assert f(None, 8, FAKE * 4, 8, 8, 8, 4, None) == tla.ERR_INVALID_ARG
+    assert f(FAKE, 7, FAKE * 4, 8, 8, 8, 4, None) == tla.ERR_INVALID_ARG  # ld_src < N
+    assert f(FAKE, 8, FAKE * 4, 7, 8, 8, 4, None) == tla.ERR_INVALID_ARG  # ld_dst < N
+    assert f(FAKE + 2, 8, FAKE * 4, 8, 8, 8, 4, None) == tla.ERR_INVALID_ARG  # misaligned
+    assert f(FAKE, 8, FAKE + 64, 8, 8, 8, 4, None) == tla.ERR_OVERLAP
+
+
 def _eval_desc(d):
     shape, stride = tla.layout_tuple(d)
     return L.Layout(shape, stride)

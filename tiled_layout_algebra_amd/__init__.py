@@ -26,7 +26,7 @@ MAX_MODES, MAX_LEAVES = 8, 16
 EXPORTED = [
     "tla_gemm_epilogue", "tla_gemm_variant", "tla_gemm_run_variant", "tla_gemm_variant_info",
     "tla_conv2d_fprop",
-    "tla_tiled_transpose", "tla_layout_size",
+    "tla_tiled_transpose", "tla_tiled_copy", "tla_layout_size",
     "tla_layout_eval", "tla_logical_divide", "tla_tiled_divide", "tla_thread_map",
     "tla_thread_map_eval", "tla_logical_product", "tla_coalesce", "tla_composition",
     "tla_logical_divide_modes", "tla_thread_map_ex", "tla_thread_map_eval_ex",
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
         L.tla_conv2d_fprop.argtypes = [ctypes.POINTER(ConvArgs), P]
         L.tla_gemm_variant_info.argtypes = [I32, I32, ctypes.POINTER(GemmKernelInfo)]
         L.tla_tiled_transpose.argtypes = [P, I64, P, I64, I64, I64, I32, P]
+        L.tla_tiled_copy.argtypes = [P, I64, P, I64, I64, I64, I32, P]
         L.tla_layout_size.argtypes = [LP, ctypes.POINTER(I64)]
         L.tla_layout_eval.argtypes = [LP, LP, P, I64, P]
         L.tla_logical_divide.argtypes = [LP, ctypes.POINTER(I64), I32, LP]
@@ -238,6 +239,12 @@ def tiled_transpose(src, ld_src, dst, ld_dst, M, N, elem_bytes, stream=None):
     _check(lib().tla_tiled_transpose(_dev(src, "src"), ld_src, _dev(dst, "dst"), ld_dst, M, N,
                                      elem_bytes, _stream(stream, src, dst)),
            "tla_tiled_transpose")
+
+
+def tiled_copy(src, ld_src, dst, ld_dst, M, N, elem_bytes, stream=None):
+    """dst[m*ld_dst + n] = src[m*ld_src + n], raw bits (tla_tiled_copy)."""
+    _check(lib().tla_tiled_copy(_dev(src, "src"), ld_src, _dev(dst, "dst"), ld_dst, M, N,
+                                elem_bytes, _stream(stream, src, dst)), "tla_tiled_copy")
 
 
 # ---------------------------------------------------------------- layouts

@@ -262,6 +262,21 @@ int tla_tiled_transpose(const void* src, int64_t ld_src, void* dst, int64_t ld_d
   return transpose_dispatch(src, ld_src, dst, ld_dst, M, N, elem_bytes, (hipStream_t)stream);
 }
 
+int tla_tiled_copy(const void* src, int64_t ld_src, void* dst, int64_t ld_dst, int64_t M,
+                   int64_t N, int32_t elem_bytes, void* stream) {
+  if (M < 0 || N < 0) return TLA_ERR_INVALID_ARG;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8 && elem_bytes != 16)
+    return TLA_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return TLA_OK;
+  if (!src || !dst || ld_src < N || ld_dst < N) return TLA_ERR_INVALID_ARG;
+  if (((uintptr_t)src % (uintptr_t)elem_bytes) || ((uintptr_t)dst % (uintptr_t)elem_bytes))
+    return TLA_ERR_INVALID_ARG;
+  const uintptr_t s0 = (uintptr_t)src, s1 = s0 + (uintptr_t)(((M - 1) * ld_src + N) * elem_bytes);
+  const uintptr_t d0 = (uintptr_t)dst, d1 = d0 + (uintptr_t)(((M - 1) * ld_dst + N) * elem_bytes);
+  if (s0 < d1 && d0 < s1) return TLA_ERR_OVERLAP;
+  return copy_dispatch(src, ld_src, dst, ld_dst, M, N, elem_bytes, (hipStream_t)stream);
+}
+
 int tla_layout_size(const tla_layout* L, int64_t* size) {
   if (!size) return TLA_ERR_INVALID_ARG;
   FlatLayout f;

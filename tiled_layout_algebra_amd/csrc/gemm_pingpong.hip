@@ -11,25 +11,21 @@
 // kt and kt+1 (section 四: pipeline stages hide the global-memory latency).
 //
 // Schedule.  A gfx950 workgroup of eight waves places waves w and w+4 on the
-// same SIMD, one from each group.  Time is cut into phases separated by
-// workgroup barriers; in every phase one group only issues MFMAs from
-// fragments it already holds in registers (a whole k-tile of them), while
-// the other reads its next k-tile's fragments from LDS and issues the
-// direct HBM -> LDS copies of a later k-tile.  Each SIMD therefore always
-// has one wave with a full k-tile of independent matrix instructions ready,
-// and no copy instruction sits between MFMAs: under load a direct-to-LDS
-// copy holds its wave's in-order issue for about a hundred cycles.
-//
-//   phase 2kt   : group 0 multiplies k-tile kt;  group 1 reads kt's
-//                 fragments and copies B of k-tile kt+2
-//   phase 2kt+1 : group 1 multiplies k-tile kt;  group 0 reads kt+1's
-//                 fragments and copies A of k-tile kt+2
+// same SIMD, one from each group.  Each group alternates a memory phase
+// (read one k-tile's fragments from LDS into registers, issue the direct
+// HBM -> LDS copies of a later k-tile) with a compute phase (a whole
+// k-tile of MFMAs from registers), and the two groups are half a period
+// apart, held there by workgroup barriers: group 0 starts a period with its
+// memory phase, group 1 with its compute phase.  So on each SIMD one wave
+// multiplies while the other moves data, and no copy instruction sits
+// between MFMAs: under load a direct-to-LDS copy holds its wave's in-order
+// issue for about a hundred cycles.
 //
 // LDS holds two A slabs and three B slabs (5 x 32 KiB = the whole 160 KiB):
 // B of k-tile kt+2 is copied while k-tiles kt and kt+1 are both still
-// live.  Each group waits for its own copies before the barrier that ends
-// the phase before their first reader.  After the last barrier group 0 runs
-// its epilogue while group 1 still multiplies the last k-tile.
+// live.  Each group waits for its own copies before the barrier that
+// precedes their first reader.  After the last barrier group 0 runs its
+// epilogue while group 1 still multiplies the last k-tile.
 //
 // Copies are raw buffer loads straight into LDS.  Copy q of a thread moves
 // 16 bytes of slab row r0 + 32q (r0 = thread / 8): the buffer resource starts
@@ -192,27 +188,34 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Each group runs its own program, a loop of (memory phase, compute
-  // phase) with exactly one MFMA sequence; copies are issued only in memory
-  // phases.  Both programs pass the same number of barriers: group 1 starts
-  // one phase later, so its loop has one barrier less at the end and its
-  // prologue one more.
-  //   group 0, phase 2kt-1: read k-tile kt's fragments; copy A of kt+1 into
-  //     A slot (kt+1)%2 (it held kt-1, read in phases 2kt-3 and 2kt-2);
-  //     phase 2kt: multiply kt, then wait for A of kt+1 (read in 2kt+1).
-  //   group 1, phase 2kt: read k-tile kt's fragments; copy B of kt+2 into
-  //     B slot (kt+2)%3 (it held kt-1); wait for B of kt+1 (read in 2kt+1);
-  //     phase 2kt+1: multiply kt.
+  // Each group runs its own program with exactly one MFMA sequence; copies
+  // are issued only between LDS reads.  Period kt ends at barrier kt:
+  //   group 0: read k-tile kt's fragments and copy A of kt+1 into A slot
+  //     (kt+1)%2 (it held kt-1, read by both groups in period kt-1), then
+  //     multiply kt and wait for its copies;
+  //   group 1: multiply kt-1 (fragments read in period kt-1), then read
+  //     kt's fragments and copy B of kt+2 into B slot (kt+2)%3 (it held
+  //     kt-1), then wait for B of kt+1 (copied in period kt-1); in period
+  //     0 it only reads.
+  // Every slab is thus complete one barrier before its first reader.  With
+  // 16-bit operands a second barrier splits each period between the two
+  // halves (group 0 reads while group 1 multiplies, then the other way
+  // round): a 16-bit MFMA holds its wave's issue for its whole run, and
+  // without the split group 0 starts multiplying before group 1 is done, so
+  // both share the matrix core and the period grows (3084 cycles per k-tile
+  // against 2508).  e4m3 MFMAs queue without holding issue, and there one
+  // barrier per period measured 2892 cycles against 3728.
+  constexpr bool kSplit = kSub == 1;
   if (KT > 0) {
     if (grp == 0) {
       copy_slab(0, 0, true);
       wait_vmcnt<0>();
       barrier();
       for (int kt = 0; kt < KT; ++kt) {
-        memory_phase(kt, kt + 1, (kt + 1) & 1, kt + 1 < KT);  // phase 2kt-1
+        memory_phase(kt, kt + 1, (kt + 1) & 1, kt + 1 < KT);
         wait_lgkmcnt0();
-        barrier();
-        compute();                                   // phase 2kt
+        if constexpr (kSplit) barrier();
+        compute();
         wait_vmcnt<0>();                             // A of kt+1 landed
         barrier();
       }
@@ -221,14 +224,18 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
       copy_slab(1, 1, KT > 1);
       wait_vmcnt<kCopies>();
       barrier();
-      barrier();                                     // phase -1
+      if constexpr (kSplit) barrier();
+      // one iteration reads k-tile kt (end of period kt) and multiplies it
+      // (start of period kt+1): the fragments never live across iterations
       for (int kt = 0; kt < KT; ++kt) {
-        memory_phase(kt, kt + 2, (kt + 2) % 3, kt + 2 < KT);  // phase 2kt
+        memory_phase(kt, kt + 2, (kt + 2) % 3, kt + 2 < KT);
         wait_lgkmcnt0();
         wait_vmcnt<kCopies>();                       // B of kt+1 landed
         barrier();
-        compute();                                   // phase 2kt+1
-        if (kt + 1 < KT) barrier();
+        compute();
+        if constexpr (kSplit) {
+          if (kt + 1 < KT) barrier();
+        }
       }
       wait_vmcnt<0>();  // the last (record-less) copies
     }

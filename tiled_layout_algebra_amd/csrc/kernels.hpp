@@ -53,6 +53,8 @@ int gemm_variant_info(int a_type, int variant, GemmKernelInfo* out);
 
 int transpose_dispatch(const void* src, int64_t ld_src, void* dst, int64_t ld_dst, int64_t M,
                        int64_t N, int elem_bytes, hipStream_t stream);
+int copy_dispatch(const void* src, int64_t ld_src, void* dst, int64_t ld_dst, int64_t M,
+                  int64_t N, int elem_bytes, hipStream_t stream);
 
 // Flat leaf lists of (validated) layouts; inner_leaves == 0 means no inner.
 struct FlatLayout {
