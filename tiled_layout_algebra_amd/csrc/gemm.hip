@@ -1,33 +1,32 @@
-// gemm.hip -- hierarchically tiled GEMM with a fused epilogue for gfx950.
+// gemm.hip -- the single-group GEMM kernels (128 x 128 and 256 x 256 block
+// tiles, direct-to-LDS or register-staged loads), the implicit-GEMM
+// convolution and the variant dispatch, for gfx950.
 //
 //   D = act(alpha_eff * A.B + beta*C + bias),  fp32 accumulation.
 //
 // Three levels of tiling, as in "CUTLASS / CuTe 主线" (hpc.payai.win/cutlass),
 // section 一: a workgroup owns a BM x BN tile of D (the block tile), each of
-// its four 64-lane wavefronts a (BM/2) x (BN/2) quarter (the wave tile), and
-// each 32x32 MFMA instruction a 32x32 piece of that (the instruction tile).
-// The K loop (section 二's mainloop: global -> shared -> register) moves one
-// 128-byte-wide K slab of A and of B per step into LDS (64 bf16/fp16 or 128
-// e4m3 per row), double-buffered so the next slab streams in while the
-// current one feeds the matrix cores (section 四: pipeline stages hide global
-// latency).  The epilogue applies alpha, beta*C, bias and the activation to
-// the fp32 accumulators in registers and stores D once (section 四: fuse
-// before the store); for whole tiles the freed LDS stages turn C and D into
-// whole-row transfers (see epilogue_lds).
-//
-// Operand roles.  Both LDS slabs hold rows of K (A by m, B by n).  The MFMA
-// is issued with the B rows as its first operand and the A rows as its
-// second, so its 32x32 result is D^T: each lane then owns four consecutive
-// columns of one row of D, which the epilogue reads (C) and writes (D) as
-// 8-byte vectors.
+// its 64-lane wavefronts a piece of it (the wave tile: 2 x 4 waves of
+// (BM/2) x (BN/4) in gemm_fast_kernel with 16-bit operands, 2 x 2 waves of
+// (BM/2) x (BN/2) in gemm_kernel, which serves e4m3, the register-staged
+// general path and the convolution), and each 32x32 MFMA instruction a
+// 32x32 piece of that (the instruction tile).  The K loop (section 二's
+// mainloop: global -> shared -> register) moves one 128-byte-wide K slab of
+// A and of B per step into LDS (64 bf16/fp16 or 128 e4m3 per row), with two
+// or three stages so the next slab streams in while the current one feeds
+// the matrix cores (section 四: pipeline stages hide global latency).  The
+// epilogue (gemm_common.hpp) applies alpha, beta*C, bias and the activation
+// to the fp32 accumulators in registers and stores D once (section 四: fuse
+// before the store).  The two-group 256 x 256 kernel the dispatch prefers
+// for large problems lives in gemm_pingpong.hip.
 //
 // Two load paths feed the same LDS layout:
 //   fast    both operands K-contiguous, 16-byte aligned rows, K a multiple of
-//           the slab width: each lane issues global_load_lds_dwordx4, a
-//           direct HBM -> LDS copy that lands lane-linearly; the LDS XOR
-//           swizzle is applied by permuting which global chunk each lane
-//           fetches.  Rows past M or N are clamped to the last real row (their
-//           results are never stored), so the loop carries no predicates.
+//           the slab width: each lane issues a direct HBM -> LDS copy that
+//           lands lane-linearly; the LDS XOR swizzle is applied by permuting
+//           which global chunk each lane fetches.  Rows past M or N are
+//           clamped to the last real row (their results are never stored),
+//           so the loop carries no predicates.
 //   general any order, pitch or alignment, ragged K: registers staged through
 //           a strip-mined thread map with per-element predicates; elements
 //           outside the matrix load as zero.
