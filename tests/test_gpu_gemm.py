@@ -314,6 +314,41 @@ def test_forced_variants_random_inputs(variant):
     _check_full(case, W.gemm_inputs(case), variant=variant)
 
 
+def _ulp(v, d_type):
+    """Spacing of D's type at |v| (the least subnormal at 0)."""
+    v = np.abs(v)
+    if d_type == W.F16:
+        return np.spacing(v.astype(np.float16)).astype(np.float64)
+    _, e = np.frexp(np.maximum(v, 2.0 ** -126))
+    return np.ldexp(1.0, e - 8)
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+@pytest.mark.parametrize("d_type,c_type", [(W.BF16, W.BF16), (W.F16, W.F16), (W.BF16, W.F32)])
+def test_gelu_activation_accuracy(variant, d_type, c_type):
+    """D = GELU(C) (A = 0, beta = 1) over y in [-9, 9] on every variant and
+    both epilogue forms (16-bit C through the tile epilogue, fp32 C through
+    the per-group one): within half an output ulp of the exact y * Phi(y)
+    plus 4e-7 (1 + |y|) of fp32 evaluation error."""
+    M, N, K = 512, 512, 128
+    a_type = W.F16 if d_type == W.F16 else W.BF16
+    case = W.GemmCase(name="gelu", M=M, N=N, K=K, a_type=a_type, b_type=a_type, d_type=d_type,
+                      c_type=c_type, alpha=1.0, beta=1.0, act=W.ACT_GELU, has_c=True, seed=93)
+    inp = W.gemm_inputs(case)
+    inp["A"] = np.zeros_like(inp["A"])
+    inp["B"] = np.zeros_like(inp["B"])
+    inp["C"] = W.encode(np.linspace(-9.0, 9.0, M * N), c_type).reshape(-1)
+    y = og.decode(c_type, inp["C"].copy()).reshape(M, N)
+    D = G.run_gemm(case, inp, sentinel=SENT[d_type], variant=variant)
+    got = _logical(case, D)
+    ref = G.oracle_ref(case, inp)
+    bound = 0.5 * _ulp(np.maximum(np.abs(got), np.abs(ref)), d_type) + 4e-7 * (1 + np.abs(y))
+    err = np.abs(got - ref)
+    assert not np.isnan(got).any()
+    assert (err <= bound).all(), "worst excess %g at y = %g" % (
+        (err - bound).max(), y.flat[np.argmax(err - bound)])
+
+
 def test_forced_fast_variant_refuses_general_layout():
     import tiled_layout_algebra_amd as tla
     case = _small(b_order=W.ROW)  # B N-contiguous: no fast layout

@@ -316,9 +316,34 @@ __device__ __forceinline__ void load4(const uint8_t* p, int type, int64_t idx, f
   }
 }
 
+// GELU(y) = y * Phi(y), Phi the standard normal distribution function, in
+// erfc form: with h = erfc(a) / 2, a = |y| / sqrt(2), Phi(y) is 1 - h for
+// y >= 0 and h for y < 0, so GELU(y) = max(y, 0) - |y| h.
+// erfc(a) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^(-a^2), t = 1 / (1 + p a),
+// is formula 7.1.26 of Abramowitz and Stegun, Handbook of Mathematical
+// Functions (|error| <= 1.5e-7).  Here the coefficients are halved and the
+// argument is b = a sqrt(log2 e), so that e^(-a^2) = 2^(-b^2) and
+// p a = (p / sqrt(log2 e)) b.  Branch-free, 14 vector operations (two of
+// them the hardware reciprocal and exp2) against about 30 with a divergent
+// branch for 1 + erf(y / sqrt 2); |Phi - exact| <= 3e-7 in fp32, the same
+// as the erf form.  |y| is clamped to the largest float so that
+// GELU(+inf) = +inf and GELU(-inf) = 0.  The epilogue applies it to every
+// accumulator, 128 per lane per tile.
+__device__ __forceinline__ float gelu(float y) {
+  const float ay = fminf(fabsf(y), 3.40282347e38f);
+  const float b = ay * 0.8493218003f;                  // |y| sqrt(log2(e) / 2)
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.2727374809f, b, 1.0f));
+  float q = fmaf(t, 0.5307027145f, -0.7265760135f);
+  q = fmaf(t, q, 0.7107068705f);
+  q = fmaf(t, q, -0.142248368f);
+  q = fmaf(t, q, 0.127414796f);
+  const float h = q * t * __builtin_amdgcn_exp2f(b * -b);
+  return fmaf(-ay, h, fmaxf(y, 0.f));
+}
+
 __device__ __forceinline__ float activate(float y, int act) {
   if (act == TLA_ACT_RELU) return y > 0.f ? y : 0.f;
-  if (act == TLA_ACT_GELU) return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f));
+  if (act == TLA_ACT_GELU) return gelu(y);
   return y;
 }
 
@@ -369,19 +394,27 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, int m, int n, con
 }
 
 // ------------------------------------------- specialised full-tile epilogue
-// The two fast epilogue paths below are compiled once per activation and
-// per D type, so the per-element work is straight-line code; C and bias
-// (bf16 or fp16) are widened with a select rather than a branch.
-__device__ __forceinline__ float widen16(uint32_t w, bool bf16) {
-  const float b = __builtin_bit_cast(float, w << 16);
-  const float h = (float)__builtin_bit_cast(_Float16, (uint16_t)w);
-  return bf16 ? b : h;
+// The two fast epilogue paths below are compiled per activation, per
+// 16-bit type (shared by C, bias and D) and with or without C, so the
+// per-element work is straight-line code: one fma for alpha*acc + bias,
+// one widening and one fma for beta*C, the activation and a packed
+// conversion.  The low and high halves of a packed pair widen in one
+// operation each.
+template <bool kBf16>
+__device__ __forceinline__ float widen_lo(uint32_t w) {
+  if constexpr (kBf16) return __builtin_bit_cast(float, w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+template <bool kBf16>
+__device__ __forceinline__ float widen_hi(uint32_t w) {
+  if constexpr (kBf16) return __builtin_bit_cast(float, w & 0xFFFF0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
 template <int kAct>
 __device__ __forceinline__ float act_t(float y) {
   if constexpr (kAct == TLA_ACT_RELU) return y > 0.f ? y : 0.f;
-  if constexpr (kAct == TLA_ACT_GELU) return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f));
+  if constexpr (kAct == TLA_ACT_GELU) return gelu(y);
   return y;
 }
 
@@ -395,21 +428,26 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
-// y = act(alpha*acc + beta*c + bias) for the four values of group g of tile
-// (i, j); c and bias arrive as packed 16-bit pairs.
-template <int kAct, bool kDBf16>
+// y = act(alpha*acc + bias + beta*c) for the four values of group g of tile
+// (i, j); c and bias arrive as packed 16-bit pairs (bias zero bits when
+// there is none).
+template <int kAct, bool kBf16, bool kHasC>
 __device__ __forceinline__ uint2 epi_group(const f32x16& acc, int g, uint2 c, uint2 b, float alpha,
-                                           float beta, bool c_bf16, bool b_bf16) {
-  const uint32_t cw[4] = {c.x, c.x >> 16, c.y, c.y >> 16};
-  const uint32_t bw[4] = {b.x, b.x >> 16, b.y, b.y >> 16};
+                                           float beta) {
+  const float bias[4] = {widen_lo<kBf16>(b.x), widen_hi<kBf16>(b.x), widen_lo<kBf16>(b.y),
+                         widen_hi<kBf16>(b.y)};
   float y[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float v = alpha * acc[4 * g + q];
-    v += beta * widen16(cw[q] & 0xFFFFu, c_bf16);
-    y[q] = act_t<kAct>(v + widen16(bw[q] & 0xFFFFu, b_bf16));
+  for (int q = 0; q < 4; ++q) y[q] = fmaf(alpha, acc[4 * g + q], bias[q]);
+  if constexpr (kHasC) {
+    y[0] = fmaf(beta, widen_lo<kBf16>(c.x), y[0]);
+    y[1] = fmaf(beta, widen_hi<kBf16>(c.x), y[1]);
+    y[2] = fmaf(beta, widen_lo<kBf16>(c.y), y[2]);
+    y[3] = fmaf(beta, widen_hi<kBf16>(c.y), y[3]);
   }
-  return uint2{pack2<kDBf16>(y[0], y[1]), pack2<kDBf16>(y[2], y[3])};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) y[q] = act_t<kAct>(y[q]);
+  return uint2{pack2<kBf16>(y[0], y[1]), pack2<kBf16>(y[2], y[3])};
 }
 
 // This lane's 16-bit bias values for its column groups, all loads issued
@@ -432,7 +470,7 @@ __device__ __forceinline__ void load_bias16(const GemmParams& p, int n_base, int
 // back in place and stores D from LDS as whole rows.  The region's 16-byte
 // chunks are XOR-swizzled by row so that the lane-per-row accesses of one
 // instruction fall into distinct LDS banks.
-template <int kAct, bool kDBf16, int FM, int FN>
+template <int kAct, bool kDBf16, bool kHasC, int FM, int FN>
 __device__ __forceinline__ void epilogue_lds(const GemmParams& p, int m_base, int n_base, int lane,
                                              const f32x16 (&acc)[FM][FN], uint8_t* region) {
   constexpr int kRowB = 64 * FN, kCh = kRowB / 16, kRowsPerKiB = 1024 / kRowB;
@@ -441,8 +479,7 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, int m_base, in
   auto swz = [](int r, int c) { return c ^ ((r / (16 / kCh)) & (kCh - 1)); };
   const int row = lane & 31, half = lane >> 5;
   const int rr = lane / kCh, cs = lane % kCh;  // row-wise view of one KiB
-  const bool has_c = p.beta != 0.f;
-  if (has_c) {
+  if constexpr (kHasC) {
     const uint8_t* C = p.C + ((int64_t)m_base * p.c_sm + n_base) * 2;
     static_for<kIters>([&](auto t) {
       const int r = kRowsPerKiB * t + rr;
@@ -454,15 +491,13 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, int m_base, in
   load_bias16<FN>(p, n_base, half, braw);
   wait_vmcnt<0>();  // this wave's C copies have landed in its region
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const bool c_bf16 = p.c_type == kBF16, b_bf16 = p.bias_type == kBF16;
-  const float beta = has_c ? p.beta : 0.f;
   static_for<FM>([&](auto i) {
     static_for<FN>([&](auto j) {
       static_for<4>([&](auto g) {
         const int r = 32 * i + row;
         uint8_t* slot = region + r * kRowB + swz(r, 4 * j + g) * 16 + 8 * half;
-        const uint2 c = has_c ? *(const uint2*)slot : uint2{0u, 0u};
-        *(uint2*)slot = epi_group<kAct, kDBf16>(acc[i][j], g, c, braw[j][g], p.alpha, beta, c_bf16, b_bf16);
+        const uint2 c = kHasC ? *(const uint2*)slot : uint2{0u, 0u};
+        *(uint2*)slot = epi_group<kAct, kDBf16, kHasC>(acc[i][j], g, c, braw[j][g], p.alpha, p.beta);
       });
     });
   });
@@ -476,13 +511,12 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, int m_base, in
 
 // Full wave tile straight from and to global memory with 8-byte vectors;
 // all C and bias loads are issued before the arithmetic.
-template <int kAct, bool kDBf16, int FM, int FN>
+template <int kAct, bool kDBf16, bool kHasC, int FM, int FN>
 __device__ __forceinline__ void epilogue_direct(const GemmParams& p, int m_base, int n_base, int lane,
                                                 const f32x16 (&acc)[FM][FN]) {
   const int row = lane & 31, half = lane >> 5;
-  const bool has_c = p.beta != 0.f;
   uint2 c[FM][FN][4];
-  if (has_c) {
+  if constexpr (kHasC) {
     const uint16_t* C = (const uint16_t*)p.C;
     static_for<FM>([&](auto i) {
       static_for<FN>([&](auto j) {
@@ -499,14 +533,12 @@ __device__ __forceinline__ void epilogue_direct(const GemmParams& p, int m_base,
   }
   uint2 braw[FN][4];
   load_bias16<FN>(p, n_base, half, braw);
-  const bool c_bf16 = p.c_type == kBF16, b_bf16 = p.bias_type == kBF16;
-  const float beta = has_c ? p.beta : 0.f;
   uint16_t* D = (uint16_t*)p.D;
   static_for<FM>([&](auto i) {
     static_for<FN>([&](auto j) {
       static_for<4>([&](auto g) {
         *(uint2*)(D + (int64_t)(m_base + 32 * i + row) * p.d_sm + n_base + 32 * j + 8 * g + 4 * half) =
-            epi_group<kAct, kDBf16>(acc[i][j], g, c[i][j][g], braw[j][g], p.alpha, beta, c_bf16, b_bf16);
+            epi_group<kAct, kDBf16, kHasC>(acc[i][j], g, c[i][j][g], braw[j][g], p.alpha, p.beta);
       });
     });
   });
@@ -515,10 +547,14 @@ __device__ __forceinline__ void epilogue_direct(const GemmParams& p, int m_base,
 template <bool kLds, int kAct, bool kDBf16, int FM, int FN>
 __device__ __forceinline__ void epilogue_fast(const GemmParams& p, int m_base, int n_base, int lane,
                                               const f32x16 (&acc)[FM][FN], uint8_t* region) {
-  if constexpr (kLds)
-    epilogue_lds<kAct, kDBf16, FM, FN>(p, m_base, n_base, lane, acc, region);
-  else
-    epilogue_direct<kAct, kDBf16, FM, FN>(p, m_base, n_base, lane, acc);
+  const bool has_c = p.beta != 0.f;
+  if constexpr (kLds) {
+    if (has_c) epilogue_lds<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc, region);
+    else epilogue_lds<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc, region);
+  } else {
+    if (has_c) epilogue_direct<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc);
+    else epilogue_direct<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc);
+  }
 }
 
 template <bool kLds, int FM, int FN>
@@ -545,16 +581,17 @@ __device__ __forceinline__ void epilogue_switch(const GemmParams& p, int m_base,
 // rows m_base + 32i + lane%32, column groups n_base + 32j + 8g + 4(lane/32).
 // `region` is this wave's 32*FM x 64*FN-byte piece of LDS, free for reuse
 // (the caller has synchronised the workgroup after its last LDS read), or
-// null.  A wave tile inside D with 16-bit C (or no C) and bias takes the LDS
-// path when C and D rows allow 16-byte vectors, else the direct path with
-// 8-byte vectors; anything else (edge tiles, fp32 C or bias, strided C or D)
-// goes group by group through the predicated epilogue4.
+// null.  A wave tile inside D whose C (if any) and bias (if any) have D's
+// 16-bit type takes the LDS path when C and D rows allow 16-byte vectors,
+// else the direct path with 8-byte vectors; anything else (edge tiles, fp32
+// or mixed-type C or bias, strided C or D) goes group by group through the
+// predicated epilogue4.
 template <int FM, int FN>
 __device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, int n_base, int lane,
                                                const f32x16 (&acc)[FM][FN], uint8_t* region) {
   const bool full = m_base + 32 * FM <= p.M && n_base + 32 * FN <= p.N;
-  const bool b_ok = !p.bias || ((p.flags & kBiasVec) && p.bias_type != kF32);
-  const bool c16 = p.c_type != kF32;
+  const bool b_ok = !p.bias || ((p.flags & kBiasVec) && p.bias_type == p.d_type);
+  const bool c16 = p.c_type == p.d_type;
   if (full && b_ok && region && (p.flags & kD16) && (p.beta == 0.f || (c16 && (p.flags & kC16)))) {
     epilogue_switch<true, FM, FN>(p, m_base, n_base, lane, acc, region);
   } else if (full && b_ok && (p.flags & kDVec) && (p.beta == 0.f || (c16 && (p.flags & kCVec)))) {
