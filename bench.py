@@ -455,7 +455,7 @@ def main():
                              kernel_counters("gemm_pingpong_kernel<bf16>", GEMM_SOURCES)),
         "transpose": {"value": round(tr_gbs, 1), "unit": "GB/s",
                       "roofline": roofline(tr_gbs, PEAK_HBM_GBS, "hbm", "GB/s", t_tr,
-                                           kernel_counters("transpose4_kernel<1,4>",
+                                           kernel_counters("transpose_lds_kernel<256,64>",
                                                            TRANSPOSE_SOURCES))},
     }
     # The identity-layout copy of the same matrix (same bytes, unit-stride

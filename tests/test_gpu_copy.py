@@ -62,6 +62,14 @@ def test_copy_misaligned_bases(eb):
                            seed=3), pad_front=1)
 
 
+@pytest.mark.parametrize("eb,pad_front", [(4, 0), (4, 1)])
+def test_copy_more_rows_than_one_grid_column(eb, pad_front):
+    """131075 rows: the rows go out in launches of at most 65535 (the grid's
+    y limit), with the 16-byte path and the element-wise one."""
+    _check(W.TransposeCase(name="c", M=131075, N=12, ld_src=16, ld_dst=20, elem_bytes=eb,
+                           seed=5), pad_front=pad_front)
+
+
 def test_copy_full_size_fp32_bits():
     tc = W.TRANSPOSE_F32_16384
     case = W.TransposeCase(name="copy", M=tc.M, N=tc.N, ld_src=tc.N, ld_dst=tc.N, seed=tc.seed)

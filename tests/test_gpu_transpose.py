@@ -49,7 +49,8 @@ def _oracle(case, src_bits, dst0):
 
 SHAPES = [(1, 1, 0, 0), (3, 5, 0, 0), (32, 32, 0, 0), (33, 65, 0, 0), (100, 37, 3, 1),
           (64, 64, 0, 0), (128, 256, 0, 0), (256, 1024, 0, 0), (260, 516, 0, 0),
-          (64, 48, 4, 8), (63, 64, 0, 0), (129, 131, 7, 5)]
+          (64, 48, 4, 8), (63, 64, 0, 0), (129, 131, 7, 5), (4, 4, 0, 0), (256, 64, 0, 0),
+          (516, 260, 0, 0), (300, 68, 8, 4), (1028, 196, 4, 12)]
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])

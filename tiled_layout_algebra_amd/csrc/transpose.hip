@@ -11,15 +11,15 @@
 // element per thread per access); here both sides move whole cache lines:
 //
 //   fast path (4-byte elements, M and N multiples of 4, 16-byte aligned rows
-//   and columns): the 64 x 256 block tile is cut into 4x4 micro-tiles; a
-//   thread loads its micro-tile as four 16-byte row vectors, transposes it
-//   in registers and stores four 16-byte column vectors.  Lanes are laid out
-//   8 x 8 over micro-tiles, so every wavefront load and store covers
-//   128-byte runs -- whole cache lines on both sides, no LDS.  All of a
-//   thread's loads are issued before any store; whole tiles carry no
-//   predicate at all (one exec-mask branch per access measured 416.8 us
-//   against 394 us on a 16384^2 fp32 transpose), edge tiles check each
-//   micro-tile.
+//   and columns): 256 x 64 block tiles, staged through LDS.  A thread loads
+//   4x4 micro-tiles as four 16-byte row vectors, 16 lanes side by side along
+//   each source row (256-byte runs), transposes each micro-tile in registers
+//   and writes its four 16-byte column pieces into LDS, which holds the tile
+//   column by column; then 64 lanes read one whole LDS column each and store
+//   it as a 1 KiB run of a destination column.  Tiles are launched tile row
+//   fastest, so consecutive workgroups continue the same destination
+//   columns.  All of a thread's loads are issued before any store; whole
+//   tiles carry no predicate, edge tiles check each micro-tile and chunk.
 //
 //   general path (1/2/4/8/16-byte elements, any pitch, ragged edges): a
 //   32 x 32 tile staged through a padded LDS tile.  The strip-mined thread
@@ -38,63 +38,74 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ----------------------------------------------------------------- fast path
-// One thread's TI x TJ micro-tiles: rows 4*(mi + 16a), columns 4*(mj + 16b)
-// of the block tile, lanes 8 x 8 per wave, waves 2 x 2.
-template <int TI, int TJ, bool kEdge>
-__device__ __forceinline__ void transpose_micro(const uint32_t* __restrict__ s, int64_t ld_src,
-                                                uint32_t* __restrict__ d, int64_t ld_dst,
-                                                int64_t rows_left, int64_t cols_left, int mi,
-                                                int mj) {
-  u32x4 v[TI][TJ][4];
+// Block tile TM x TN of 4-byte elements, 256 threads.  Load: thread t owns
+// micro-tile column mj = t % NT and micro-tile rows t / NT + k * (256 / NT).
+// LDS: TN rows (one per tile column) of MT 16-byte chunks (chunk i = tile
+// rows 4i..4i+3), chunk i of row c stored at position i ^ ((c / 4) % MT): the
+// 16 lanes of one write phase then hit 16 distinct bank groups, and a row
+// stays a permutation of its chunks for the conflict-free read.  Store:
+// thread t moves chunk t % MT of LDS rows t / MT + k * (256 / MT).
+template <int TM, int TN, bool kEdge>
+__device__ __forceinline__ void transpose_tile(const uint32_t* __restrict__ s, int64_t ld_src,
+                                               uint32_t* __restrict__ d, int64_t ld_dst,
+                                               int64_t rows_left, int64_t cols_left,
+                                               u32x4* __restrict__ lds) {
+  constexpr int MT = TM / 4, NT = TN / 4, P = MT * NT / 256;
+  constexpr int RPP = 256 / NT, CPP = 256 / MT;
+  static_assert(P * 256 == MT * NT && RPP * NT == 256 && CPP * MT == 256 && 4 * P * CPP == TN,
+                "tile geometry");
+  static_assert((MT & (MT - 1)) == 0, "the chunk swizzle needs a power-of-two row");
+  const int t = threadIdx.x;
+  const int mj = t % NT, mi0 = t / NT;
+  u32x4 v[P][4];
 #pragma unroll
-  for (int a = 0; a < TI; ++a)
+  for (int k = 0; k < P; ++k) {
+    const int r = 4 * (mi0 + k * RPP), c = 4 * mj;
+    if (kEdge && !(r < rows_left && c < cols_left)) continue;
 #pragma unroll
-    for (int b = 0; b < TJ; ++b) {
-      const int r = 4 * (mi + 16 * a), c = 4 * (mj + 16 * b);
-      if (kEdge && !(r < rows_left && c < cols_left)) continue;
+    for (int q = 0; q < 4; ++q)
+      v[k][q] = __builtin_nontemporal_load((const u32x4*)(s + (r + q) * ld_src + c));
+  }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        v[a][b][q] = __builtin_nontemporal_load((const u32x4*)(s + (r + q) * ld_src + c));
+  for (int k = 0; k < P; ++k) {
+    const int mi = mi0 + k * RPP;
+    const u32x4* x = v[k];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = 4 * mj + q;
+      lds[c * MT + (mi ^ ((c >> 2) & (MT - 1)))] = u32x4{x[0][q], x[1][q], x[2][q], x[3][q]};
     }
+  }
+  __syncthreads();
+  const int j = t % MT, c0 = t / MT;
 #pragma unroll
-  for (int a = 0; a < TI; ++a)
-#pragma unroll
-    for (int b = 0; b < TJ; ++b) {
-      const int r = 4 * (mi + 16 * a), c = 4 * (mj + 16 * b);
-      if (kEdge && !(r < rows_left && c < cols_left)) continue;
-      const u32x4* x = v[a][b];
-      const u32x4 col[4] = {{x[0][0], x[1][0], x[2][0], x[3][0]},
-                            {x[0][1], x[1][1], x[2][1], x[3][1]},
-                            {x[0][2], x[1][2], x[2][2], x[3][2]},
-                            {x[0][3], x[1][3], x[2][3], x[3][3]}};
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        __builtin_nontemporal_store(col[q], (u32x4*)(d + (c + q) * ld_dst + r));
-    }
+  for (int k = 0; k < 4 * P; ++k) {
+    const int c = c0 + k * CPP;
+    if (kEdge && !(4 * j < rows_left && c < cols_left)) continue;
+    __builtin_nontemporal_store(lds[c * MT + (j ^ ((c >> 2) & (MT - 1)))],
+                                (u32x4*)(d + c * ld_dst + 4 * j));
+  }
 }
 
-template <int TI, int TJ>
-__global__ __launch_bounds__(256) void transpose4_kernel(const uint32_t* __restrict__ src,
-                                                        int64_t ld_src, uint32_t* __restrict__ dst,
-                                                        int64_t ld_dst, int64_t M, int64_t N,
-                                                        int tiles_n) {
-  constexpr int TILE_M = 64 * TI, TILE_N = 64 * TJ;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+template <int TM, int TN>
+__global__ __launch_bounds__(256) void transpose_lds_kernel(const uint32_t* __restrict__ src,
+                                                           int64_t ld_src, uint32_t* __restrict__ dst,
+                                                           int64_t ld_dst, int64_t M, int64_t N,
+                                                           int tiles_m) {
+  __shared__ u32x4 lds[TN * (TM / 4)];
+  const int tn = blockIdx.x / tiles_m, tm = blockIdx.x - tn * tiles_m;
   // this block's tile of both layouts: the tile origins are scalars, the
   // inside-tile strides are (ld_src, 1) and (1, ld_dst)
-  const int64_t blk[2] = {TILE_M, TILE_N};
+  const int64_t blk[2] = {TM, TN};
   const View<2, int64_t> tS = tile_slice(tiled_divide(row_major<int64_t>(M, N, ld_src), blk), (int64_t)tm, (int64_t)tn);
   const View<2, int64_t> tD = tile_slice(tiled_divide(col_major<int64_t>(M, N, ld_dst), blk), (int64_t)tm, (int64_t)tn);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int mi = (wave & 1) * 8 + (lane & 7);
-  const int mj = (wave >> 1) * 8 + (lane >> 3);
-  const int64_t rows_left = M - (int64_t)tm * TILE_M, cols_left = N - (int64_t)tn * TILE_N;
-  if (rows_left >= TILE_M && cols_left >= TILE_N)
-    transpose_micro<TI, TJ, false>(src + tS.offset, tS.layout.stride[0], dst + tD.offset,
-                                   tD.layout.stride[1], rows_left, cols_left, mi, mj);
+  const int64_t rows_left = M - (int64_t)tm * TM, cols_left = N - (int64_t)tn * TN;
+  if (rows_left >= TM && cols_left >= TN)
+    transpose_tile<TM, TN, false>(src + tS.offset, tS.layout.stride[0], dst + tD.offset,
+                                  tD.layout.stride[1], rows_left, cols_left, lds);
   else
-    transpose_micro<TI, TJ, true>(src + tS.offset, tS.layout.stride[0], dst + tD.offset,
-                                  tD.layout.stride[1], rows_left, cols_left, mi, mj);
+    transpose_tile<TM, TN, true>(src + tS.offset, tS.layout.stride[0], dst + tD.offset,
+                                 tD.layout.stride[1], rows_left, cols_left, lds);
 }
 
 // -------------------------------------------------------------- general path
@@ -128,16 +139,17 @@ __global__ __launch_bounds__(256) void transpose_tile32_kernel(const T* __restri
 }
 
 // ------------------------------------------------------------- 2-D copy
-// Row-major to row-major: block b copies a chunk of 256 vectors (or
-// elements) of row b / chunks, one per thread -- on a 16384^2 fp32 copy one
-// 16-byte vector per thread measured 6.55 TB/s, against 5.9-6.2 with 2 to 8
-// vectors per thread and 5.2 with 16.
+// Row-major to row-major: block (x, y) copies chunk x (256 vectors or
+// elements, one per thread) of row y.  On a 16384^2 fp32 copy this 2-D grid
+// measured 6.53-6.54 TB/s, against 6.41-6.43 with the row and chunk
+// recovered from a 1-D block index by a 64-bit division, and 6.55-6.57 for a
+// flat copy of the same contiguous bytes; one 16-byte vector per thread beat
+// 2 to 8 vectors (5.9-6.2) and 16 (5.2).
 template <typename V>
 __global__ __launch_bounds__(256) void copy_rows_kernel(const V* __restrict__ src, int64_t ld_src,
                                                        V* __restrict__ dst, int64_t ld_dst,
-                                                       int64_t row_len, int64_t chunks) {
-  const int64_t row = blockIdx.x / chunks, chunk = blockIdx.x - row * chunks;
-  const int64_t i = chunk * 256 + threadIdx.x;
+                                                       int64_t row_len) {
+  const int64_t row = blockIdx.y, i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < row_len)
     __builtin_nontemporal_store(__builtin_nontemporal_load(src + row * ld_src + i),
                                 dst + row * ld_dst + i);
@@ -163,10 +175,15 @@ template <typename V>
 int launch_copy(const void* src, int64_t ld_src, void* dst, int64_t ld_dst, int64_t M,
                 int64_t row_len, hipStream_t s) {
   const int64_t chunks = (row_len + 255) / 256;
-  if (M * chunks > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(copy_rows_kernel<V>, dim3((unsigned)(M * chunks)), dim3(256), 0, s,
-                     (const V*)src, ld_src, (V*)dst, ld_dst, row_len, chunks);
-  return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
+  if (chunks > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
+  // rows in batches of at most 65535, the grid's y limit
+  for (int64_t r0 = 0; r0 < M; r0 += 65535) {
+    const int64_t rows = M - r0 < 65535 ? M - r0 : 65535;
+    hipLaunchKernelGGL(copy_rows_kernel<V>, dim3((unsigned)chunks, (unsigned)rows), dim3(256), 0, s,
+                       (const V*)src + r0 * ld_src, ld_src, (V*)dst + r0 * ld_dst, ld_dst, row_len);
+    if (hipGetLastError() != hipSuccess) return TLA_ERR_HIP;
+  }
+  return TLA_OK;
 }
 
 }  // namespace
@@ -175,18 +192,20 @@ int transpose_dispatch(const void* src, int64_t ld_src, void* dst, int64_t ld_ds
                        int64_t N, int eb, hipStream_t s) {
   if (eb == 4 && M % 4 == 0 && N % 4 == 0 && ld_src % 4 == 0 && ld_dst % 4 == 0 && aligned16(src) &&
       aligned16(dst)) {
-    // a 64 x 256 block tile: 1 KiB runs per source row and 256-byte runs per
-    // destination column in each block.  On a 16384^2 fp32 transpose it was
-    // the fastest shape of the 4x4-micro-tile family (GB/s): 64x256 5455,
-    // 128x256 5230, 64x512 5254, 128x128 4801, 64x128 5023, 256x64 4306,
-    // 64x64 4211; walking tile rows fastest in launch order or laying lanes
-    // 16 x 4 lost 10-20 %.  A plain streaming copy of the same bytes runs at
-    // 6516-6553 GB/s on the same box.
-    constexpr int TI = 1, TJ = 4;
-    const int64_t tm = (M + 64 * TI - 1) / (64 * TI), tn = (N + 64 * TJ - 1) / (64 * TJ);
+    // 256 x 64 block tiles through LDS: 256-byte runs per source row, 1 KiB
+    // runs per destination column, tile rows fastest in launch order.  On a
+    // 16384^2 fp32 transpose (GB/s, a streaming copy of the same bytes
+    // 6516-6566): 256x64 6193-6232; 256x128 6083-6104; 512x64 6027-6053;
+    // 1024x32 6117; 256x32 6079; 128x128 5504-5559; 64x256 5457-5819;
+    // launched tile columns fastest, or with each XCD given a contiguous
+    // run of tiles, 256x64 drops to 4631-5330.  The register-only form
+    // (4x4 micro-tiles, 8 x 8 lanes, 128-byte runs both ways) peaked at
+    // 5481 with 64 x 256 tiles.
+    constexpr int TM = 256, TN = 64;
+    const int64_t tm = (M + TM - 1) / TM, tn = (N + TN - 1) / TN;
     if (tm * tn > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((transpose4_kernel<TI, TJ>), dim3((unsigned)(tm * tn)), dim3(256), 0, s,
-                       (const uint32_t*)src, ld_src, (uint32_t*)dst, ld_dst, M, N, (int)tn);
+    hipLaunchKernelGGL((transpose_lds_kernel<TM, TN>), dim3((unsigned)(tm * tn)), dim3(256), 0, s,
+                       (const uint32_t*)src, ld_src, (uint32_t*)dst, ld_dst, M, N, (int)tm);
     return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
   }
   switch (eb) {
