@@ -8,6 +8,8 @@ against the direct-convolution oracle on the same seeded inputs.
   taps read zeros from the buffer range check; 256 x 64 tiles up to 64
   output channels, 128 x 128 above), 1x1 and 5x5 filters, ragged
   output-channel and pixel counts, whole tiles through the LDS epilogue;
+* 64 -> 64 channels at stride 1 over padding, dilation, R != S, 1x1, 5x5
+  and wide rows;
 * random inputs with GELU within the tolerance, C aliasing y;
 * the measured layer (32 x 56 x 56 x 64, 3x3) compared in full, and the
   32 x 28 x 28 x 256 layer on sampled outputs.
@@ -65,6 +67,17 @@ GEOMETRIES = [  # N, H, W, C, K, R, S, stride, pad, dil
     (4, 16, 16, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
     (3, 9, 10, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
     (2, 8, 16, 128, 128, 3, 3, (1, 1), (1, 1), (1, 1)),
+    # 64 -> 64 channels at stride 1 (the measured layer's channel counts):
+    # no padding, dilation 2, R != S, 1x1, 5x5, wide and very wide rows;
+    # 128 input channels with whole 256 x 64 tiles
+    (2, 13, 7, 64, 64, 3, 3, (1, 1), (0, 0), (1, 1)),
+    (1, 11, 12, 64, 64, 3, 3, (1, 1), (2, 2), (2, 2)),
+    (3, 30, 17, 64, 64, 3, 1, (1, 1), (1, 0), (1, 1)),
+    (1, 6, 40, 64, 64, 1, 1, (1, 1), (0, 0), (1, 1)),
+    (1, 8, 200, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 12, 12, 64, 64, 5, 5, (1, 1), (2, 2), (1, 1)),
+    (1, 3, 600, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (4, 16, 16, 128, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
     # coordinates near 2^20 (padding, stride and dilation): taps on both sides
     # of the image, tap byte offsets that pass 2^32 on the direct-to-LDS path
     (2, 5, 32, 64, 24, 3, 1, (2**20 + 3, 1), (2**20, 0), (2**19, 1)),
@@ -95,6 +108,16 @@ def test_random_inputs_gelu_and_c_aliasing_y():
     case = W.ConvCase(name="rand", N=2, H=15, W=14, C=48, K=72, R=3, S=3, stride=(1, 2),
                       pad=(1, 1), dtype=W.BF16, alpha=0.75, beta=1.0, act=W.ACT_GELU,
                       has_c=True, has_bias=True, seed=31)
+    inp = W.conv_inputs(case)
+    ref = _oracle(case, inp)
+    _tolerance(case, _run(case, inp), ref)
+    _tolerance(case, _run(case, inp, alias=True), ref)
+
+
+def test_64_channels_random_gelu_and_c_aliasing_y():
+    case = W.ConvCase(name="rand64", N=2, H=15, W=14, C=64, K=64, R=3, S=3, pad=(1, 1),
+                      dtype=W.BF16, alpha=0.75, beta=1.0, act=W.ACT_GELU, has_c=True,
+                      has_bias=True, seed=32)
     inp = W.conv_inputs(case)
     ref = _oracle(case, inp)
     _tolerance(case, _run(case, inp), ref)
