@@ -162,12 +162,18 @@ TRANSPOSE_SOURCES = "transpose.hip"
 
 def source_sha(kernel_files):
     """First 16 hex digits of sha256 over a kernel's sources ('+'-separated
-    names under csrc/) followed by the shared headers."""
+    names under csrc/) followed by the shared headers, with comments and
+    blank lines taken out: an edit to comments alone keeps the hash."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in kernel_files.split("+") + _HEADERS:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -203,8 +203,10 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   // round): a 16-bit MFMA holds its wave's issue for its whole run, and
   // without the split group 0 starts multiplying before group 1 is done, so
   // both share the matrix core and the period grows (3084 cycles per k-tile
-  // against 2508).  e4m3 MFMAs queue without holding issue, and there one
-  // barrier per period measured 2892 cycles against 3728.
+  // against 2508).  With e4m3 operands the split measured 3664 cycles per
+  // k-tile against 2892 with one barrier per period: there a compute phase
+  // reaches the next barrier 170-320 cycles after starting and the other
+  // group's memory phase then takes about 1700 cycles.
   constexpr bool kSplit = kSub == 1;
   if (KT > 0) {
     if (grp == 0) {
