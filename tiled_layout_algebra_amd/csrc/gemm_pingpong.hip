@@ -189,7 +189,7 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   };
 
   // Each group runs its own program with exactly one MFMA sequence; copies
-  // are issued only between LDS reads.  Period kt ends at barrier kt:
+  // are issued only between LDS reads.  Period kt ends at barrier 2kt+1:
   //   group 0: read k-tile kt's fragments and copy A of kt+1 into A slot
   //     (kt+1)%2 (it held kt-1, read by both groups in period kt-1), then
   //     multiply kt and wait for its copies;
@@ -197,17 +197,20 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   //     kt's fragments and copy B of kt+2 into B slot (kt+2)%3 (it held
   //     kt-1), then wait for B of kt+1 (copied in period kt-1); in period
   //     0 it only reads.
-  // Every slab is thus complete one barrier before its first reader.  With
-  // 16-bit operands a second barrier splits each period between the two
-  // halves (group 0 reads while group 1 multiplies, then the other way
-  // round): a 16-bit MFMA holds its wave's issue for its whole run, and
-  // without the split group 0 starts multiplying before group 1 is done, so
-  // both share the matrix core and the period grows (3084 cycles per k-tile
-  // against 2508).  With e4m3 operands the split measured 3664 cycles per
-  // k-tile against 2892 with one barrier per period: there a compute phase
-  // reaches the next barrier 170-320 cycles after starting and the other
-  // group's memory phase then takes about 1700 cycles.
-  constexpr bool kSplit = kSub == 1;
+  // Every slab is thus complete one barrier before its first reader.  A
+  // second barrier splits each period between its halves: group 0 reads
+  // while group 1 multiplies, then the other way round.  An MFMA holds its
+  // wave's issue for its whole run, so without the split group 0 starts
+  // multiplying before group 1 is done, both share the matrix core and the
+  // period grows (16-bit: 3084 cycles per k-tile against 2508; the e4m3
+  // 8192^3 GEMM with GELU: 440 us with one barrier per period, 396 us with
+  // two).
+  //
+  // Group 1's second barrier is skipped after the last k-tile, and the
+  // compiler is free to sink the MFMAs, plain register arithmetic, past
+  // such a conditional barrier into the next period (it does so for e4m3,
+  // which then measured 3664 cycles per k-tile): an empty asm reading every
+  // accumulator keeps them in front of it.
   if (KT > 0) {
     if (grp == 0) {
       copy_slab(0, 0, true);
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
       for (int kt = 0; kt < KT; ++kt) {
         memory_phase(kt, kt + 1, (kt + 1) & 1, kt + 1 < KT);
         wait_lgkmcnt0();
-        if constexpr (kSplit) barrier();
+        barrier();
         compute();
         wait_vmcnt<0>();                             // A of kt+1 landed
         barrier();
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
       copy_slab(1, 1, KT > 1);
       wait_vmcnt<kCopies>();
       barrier();
-      if constexpr (kSplit) barrier();
+      barrier();
       // one iteration reads k-tile kt (end of period kt) and multiplies it
       // (start of period kt+1): the fragments never live across iterations
       for (int kt = 0; kt < KT; ++kt) {
@@ -235,9 +238,11 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
         wait_vmcnt<kCopies>();                       // B of kt+1 landed
         barrier();
         compute();
-        if constexpr (kSplit) {
-          if (kt + 1 < KT) barrier();
-        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) asm volatile("" ::"v"(acc[i][j]));
+        if (kt + 1 < KT) barrier();
       }
       wait_vmcnt<0>();  // the last (record-less) copies
     }
