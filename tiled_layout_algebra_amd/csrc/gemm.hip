@@ -552,13 +552,16 @@ int conv_dispatch(const ConvProblem& c, hipStream_t stream) {
   // workgroups share a CU and one's epilogue overlaps the other's main loop.
   // On 32 x 56 x 56 x 64 -> 64 (3x3) the 256 x 64 tile measured 19.5 us
   // against 40.5 us for three-stage 128 x 128 tiles; on 32 x 28 x 28 x 256
-  // -> 256 two stages measured 45.4 us against 52.8 us for three.
+  // -> 256 two stages measured 45.4 us against 52.8 us for three.  The
+  // 256 x 64 tile runs 8 wavefronts (4 x 2 of 64 x 32): each thread issues
+  // half the copies of the 4-wavefront form, and a wave blocked on a copy
+  // leaves its SIMD to the other wave's MFMAs (17.8 against 18.5 us).
   if (fast) {
     const bool narrow = c.K <= 64;
     if (c.type == TLA_BF16)
-      return narrow ? launch_fast<kBF16, 256, 64, 128, 2, 1, 2, 2, true>(p, stream)
+      return narrow ? launch_fast<kBF16, 256, 64, 128, 2, 1, 4, 2, true>(p, stream)
                     : launch_fast<kBF16, 128, 128, 128, 2, 1, 2, 2, true>(p, stream);
-    return narrow ? launch_fast<kF16, 256, 64, 128, 2, 1, 2, 2, true>(p, stream)
+    return narrow ? launch_fast<kF16, 256, 64, 128, 2, 1, 4, 2, true>(p, stream)
                   : launch_fast<kF16, 128, 128, 128, 2, 1, 2, 2, true>(p, stream);
   }
   int64_t grid;
