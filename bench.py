@@ -115,10 +115,15 @@ def sweep(steps, warmup):
                                  "←" if info["name"] == auto else ""))
                 print(lines[-1], file=sys.stderr, flush=True)
             del dA, dB, dD
-    # implicit-GEMM convolution (direct-to-LDS kernel: C is a multiple of 64)
-    lines += ["", "| convolution | N×H×W×C → K, R×S, stride, pad | GEMM M×N×K | µs | TFLOP/s "
-              "| % peak |", "|---|---|---|---|---|---|"]
+    # convolution: every kernel that applies, forced through
+    # tla_conv2d_fprop_variant with prepared arguments (a launch costs the
+    # host a few microseconds, less than any of these kernels)
+    lines += ["", "| convolution | N×H×W×C → K, R×S, stride, pad | GEMM M×N×K | kernel | µs "
+              "| TFLOP/s | % peak | auto |", "|---|---|---|---|---|---|---|---|"]
     for case in (W.CONV_F16_56,
+                 W.ConvCase(name="conv_f16_n32_56x56x64_k64_1x1", N=32, H=56, W=56, C=64,
+                            K=64, R=1, S=1, pad=(0, 0), dtype=W.F16, act=W.ACT_RELU,
+                            has_bias=True, seed=8),
                  W.ConvCase(name="conv_f16_n32_56x56x128_k64_3x3", N=32, H=56, W=56, C=128,
                             K=64, R=3, S=3, pad=(1, 1), dtype=W.F16, act=W.ACT_RELU,
                             has_bias=True, seed=7),
@@ -129,27 +134,32 @@ def sweep(steps, warmup):
         P, Q = case.out_hw()
         x, w, b = to_dev(inp["x"]), to_dev(inp["w"]), to_dev(inp["bias"])
         y = torch.empty(case.N * P * Q * case.K, dtype=torch.int16, device="cuda")
-
-        def run():
-            tla.conv2d_fprop(x, w, y, case.N, case.H, case.W, case.C, case.K, case.R, case.S,
-                             case.dtype, case.stride, case.pad, case.dil, bias=b,
-                             bias_type=case.dtype, act=case.act, stream=stream.cuda_stream)
-        for _ in range(warmup):
-            run()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(steps):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
+        args = tla.conv2d_args(x, w, y, case.N, case.H, case.W, case.C, case.K, case.R, case.S,
+                               case.dtype, case.stride, case.pad, case.dil, bias=b,
+                               bias_type=case.dtype, act=case.act)
         M, Kg = case.N * P * Q, case.R * case.S * case.C
-        tf = 2.0 * M * case.K * Kg / (us * 1e-6) / 1e12
-        lines.append("| %s | %d×%d×%d×%d → %d, %d×%d, %s, %s | %d×%d×%d | %.1f | %.0f | %.1f |" % (
-            case.name, case.N, case.H, case.W, case.C, case.K, case.R, case.S, case.stride,
-            case.pad, M, case.K, Kg, us, tf, 100 * tf / PEAK_BF16_TFLOPS))
-        print(lines[-1], file=sys.stderr, flush=True)
+        auto_done = False
+        for v in range(tla.CONV_VARIANTS):
+            if tla.conv2d_fprop_args(args, stream.cuda_stream, v) != tla.OK:
+                continue  # this kernel does not apply to the layer
+            for _ in range(warmup):
+                tla.conv2d_fprop_args(args, stream.cuda_stream, v)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(steps):
+                tla.conv2d_fprop_args(args, stream.cuda_stream, v)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            tf = 2.0 * M * case.K * Kg / (us * 1e-6) / 1e12
+            lines.append("| %s | %d×%d×%d×%d → %d, %d×%d, %s, %s | %d×%d×%d | %s | %.1f | %.0f "
+                         "| %.1f | %s |" % (
+                             case.name, case.N, case.H, case.W, case.C, case.K, case.R, case.S,
+                             case.stride, case.pad, M, case.K, Kg, tla.CONV_VARIANT_NAMES[v], us,
+                             tf, 100 * tf / PEAK_BF16_TFLOPS, "" if auto_done else "←"))
+            auto_done = True
+            print(lines[-1], file=sys.stderr, flush=True)
     print("\n".join(lines), flush=True)
 
 

@@ -218,6 +218,26 @@ typedef struct {
 
 int tla_conv2d_fprop(const tla_conv2d_args *args, void *stream);
 
+/* The convolution kernels, for comparison and testing:
+ *   0 "conv_slab"            64 input and 64 output channels at stride 1:
+ *                            the whole filter and the image rows of a band
+ *                            of output rows in LDS, each copied in once
+ *                            (x and w 16-byte aligned, H*W*128 < 2^31, a
+ *                            band of whole output rows fitting LDS)
+ *   1 "conv_implicit_fast"   the implicit GEMM with direct-to-LDS copies (C
+ *                            a multiple of 64, x and w 16-byte aligned, x
+ *                            and w each below 2 GiB)
+ *   2 "conv_implicit_general" the implicit GEMM with register-staged,
+ *                            predicated loads: any shape
+ * tla_conv2d_fprop picks the first one that applies;
+ * tla_conv2d_fprop_variant runs the one asked for, with the same semantics
+ * and tolerance, or returns TLA_ERR_UNSUPPORTED when the problem does not
+ * meet its conditions.  Arguments are validated as for tla_conv2d_fprop;
+ * variant ids outside [0, TLA_CONV_VARIANTS) are TLA_ERR_INVALID_ARG.
+ */
+#define TLA_CONV_VARIANTS 3
+int tla_conv2d_fprop_variant(const tla_conv2d_args *args, int32_t variant, void *stream);
+
 /* ---------------------------------------------------------- layouts */
 /*
  * A shape/stride layout with at most one level of nesting: n_modes

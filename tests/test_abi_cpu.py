@@ -250,3 +250,30 @@ def _conv(**kw):
 def test_conv_argument_errors(kw, status):
     a = _conv(**kw)
     assert tla.lib().tla_conv2d_fprop(ctypes.byref(a), None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), tla.ERR_INVALID_ARG), (dict(type=tla.E4M3), tla.ERR_UNSUPPORTED),
+    (dict(beta=0.5), tla.ERR_INVALID_ARG), (dict(N=0), tla.OK),
+])
+def test_conv_variant_validates_like_the_dispatching_call(kw, status):
+    a = _conv(**kw)
+    for v in range(tla.CONV_VARIANTS):
+        assert tla.lib().tla_conv2d_fprop_variant(ctypes.byref(a), v, None) == status
+
+
+def test_conv_variant_refusals():
+    """Variant ids outside [0, TLA_CONV_VARIANTS) are argument errors; the
+    slab kernel is refused outside 64 -> 64 channels at stride 1, and the
+    direct-to-LDS implicit GEMM when C is not a multiple of 64 -- all before
+    any device work."""
+    a = _conv()
+    for bad in (-1, tla.CONV_VARIANTS, 7):
+        assert tla.lib().tla_conv2d_fprop_variant(ctypes.byref(a), bad, None) == tla.ERR_INVALID_ARG
+    for kw in (dict(), dict(C=64, K=32), dict(C=128, K=64), dict(C=64, K=64, stride_h=2),
+               dict(C=64, K=64, x=FAKE + 8)):
+        assert tla.lib().tla_conv2d_fprop_variant(ctypes.byref(_conv(**kw)), 0, None) == \
+            tla.ERR_UNSUPPORTED, kw
+    for kw in (dict(), dict(C=96), dict(C=64, x=FAKE + 8)):
+        assert tla.lib().tla_conv2d_fprop_variant(ctypes.byref(_conv(**kw)), 1, None) == \
+            tla.ERR_UNSUPPORTED, kw

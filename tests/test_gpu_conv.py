@@ -8,8 +8,13 @@ against the direct-convolution oracle on the same seeded inputs.
   taps read zeros from the buffer range check; 256 x 64 tiles up to 64
   output channels, 128 x 128 above), 1x1 and 5x5 filters, ragged
   output-channel and pixel counts, whole tiles through the LDS epilogue;
-* 64 -> 64 channels at stride 1 over padding, dilation, R != S, 1x1, 5x5
-  and wide rows;
+* 64 -> 64 channels at stride 1 (the slab kernel: the whole filter and the
+  image rows of a band of output rows in LDS) over padding, dilation,
+  R != S, 1x1, 16 taps, a last band with fewer rows, and the shapes that
+  fall back to the implicit GEMM (5x5: the filter does not fit beside a
+  slab; rows wider than 512 pixels);
+* every kernel forced through tla_conv2d_fprop_variant on a subset, bit for
+  bit where it applies and refused where it does not;
 * random inputs with GELU within the tolerance, C aliasing y;
 * the measured layer (32 x 56 x 56 x 64, 3x3) compared in full, and the
   32 x 28 x 28 x 256 layer on sampled outputs.
@@ -35,7 +40,7 @@ def _oracle(case, inp):
                      act=case.act)
 
 
-def _run(case, inp, alias=False):
+def _run(case, inp, alias=False, variant=None):
     P, Q = case.out_hw()
     x, w = to_dev(inp["x"]), to_dev(inp["w"])
     c = to_dev(inp["C"]) if inp["C"] is not None else None
@@ -44,7 +49,8 @@ def _run(case, inp, alias=False):
                                   device="cuda")
     tla.conv2d_fprop(x, w, y, case.N, case.H, case.W, case.C, case.K, case.R, case.S,
                      case.dtype, case.stride, case.pad, case.dil, C_res=c, bias=b,
-                     bias_type=case.dtype, alpha=case.alpha, beta=case.beta, act=case.act)
+                     bias_type=case.dtype, alpha=case.alpha, beta=case.beta, act=case.act,
+                     variant=variant)
     torch.cuda.synchronize()
     return to_host(y, np.dtype(np.uint16)).reshape(case.N * P * Q, case.K)
 
@@ -78,6 +84,12 @@ GEOMETRIES = [  # N, H, W, C, K, R, S, stride, pad, dil
     (1, 12, 12, 64, 64, 5, 5, (1, 1), (2, 2), (1, 1)),
     (1, 3, 600, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
     (4, 16, 16, 128, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
+    # slab bands of two (three) output rows with a last band of one (two);
+    # 3x5 and 4x4 filters (16 taps: 128 KiB of filter beside the slab)
+    (10, 27, 27, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (40, 14, 14, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (2, 7, 9, 64, 64, 3, 5, (1, 1), (1, 2), (1, 1)),
+    (1, 6, 9, 64, 64, 4, 4, (1, 1), (3, 3), (2, 1)),
     # coordinates near 2^20 (padding, stride and dilation): taps on both sides
     # of the image, tap byte offsets that pass 2^32 on the direct-to-LDS path
     (2, 5, 32, 64, 24, 3, 1, (2**20 + 3, 1), (2**20, 0), (2**19, 1)),
@@ -97,6 +109,49 @@ def test_integer_inputs_bit_exact(geom, dtype):
     want = W.encode(_oracle(case, inp), dtype).reshape(got.shape)
     bad = np.argwhere(got != want)
     assert bad.size == 0, "%s: %d mismatches, first at %s" % (geom, len(bad), bad[0])
+
+
+FORCED = [  # N, H, W, C, K, R, S, stride, pad, dil
+    (4, 16, 16, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (10, 27, 27, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 11, 12, 64, 64, 3, 3, (1, 1), (2, 2), (2, 2)),
+    (2, 7, 9, 64, 64, 3, 5, (1, 1), (1, 2), (1, 1)),
+    (1, 6, 40, 64, 64, 1, 1, (1, 1), (0, 0), (1, 1)),
+    (2, 9, 11, 64, 24, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 10, 7, 128, 72, 3, 2, (2, 1), (1, 0), (1, 2)),
+    (2, 9, 11, 16, 24, 3, 3, (1, 1), (1, 1), (1, 1)),
+]
+
+
+def _variant_applies(v, geom):
+    N, H, Wd, C, K, R, S, st, pd, dl = geom
+    if v == 0:
+        return C == 64 and K == 64 and st == (1, 1)
+    if v == 1:
+        return C % 64 == 0
+    return True
+
+
+@pytest.mark.parametrize("variant", range(tla.CONV_VARIANTS))
+@pytest.mark.parametrize("geom", FORCED)
+def test_forced_variants_bit_exact(geom, variant):
+    """Each kernel run through tla_conv2d_fprop_variant on the integer set:
+    bit-exact where it applies, TLA_ERR_UNSUPPORTED (and y untouched)
+    where it does not."""
+    N, H, Wd, C, K, R, S, st, pd, dl = geom
+    case = W.ConvCase(name="forced", N=N, H=H, W=Wd, C=C, K=K, R=R, S=S, stride=st, pad=pd,
+                      dil=dl, dtype=W.BF16, alpha=1.5, beta=0.5, act=W.ACT_RELU, has_c=True,
+                      has_bias=True, seed=N * 1000 + H * 10 + C + variant, dist="int3",
+                      dist_bias="eighths")
+    inp = W.conv_inputs(case)
+    if not _variant_applies(variant, geom):
+        with pytest.raises(RuntimeError, match="UNSUPPORTED"):
+            _run(case, inp, variant=variant)
+        return
+    got = _run(case, inp, variant=variant)
+    want = W.encode(_oracle(case, inp), case.dtype).reshape(got.shape)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "%s v%d: %d mismatches, first at %s" % (geom, variant, len(bad), bad[0])
 
 
 def _tolerance(case, got, ref):

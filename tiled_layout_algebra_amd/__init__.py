@@ -25,7 +25,7 @@ MAX_MODES, MAX_LEAVES = 8, 16
 
 EXPORTED = [
     "tla_gemm_epilogue", "tla_gemm_variant", "tla_gemm_run_variant", "tla_gemm_variant_info",
-    "tla_conv2d_fprop",
+    "tla_conv2d_fprop", "tla_conv2d_fprop_variant",
     "tla_tiled_transpose", "tla_tiled_copy", "tla_layout_size",
     "tla_layout_eval", "tla_logical_divide", "tla_tiled_divide", "tla_thread_map",
     "tla_thread_map_eval", "tla_logical_product", "tla_coalesce", "tla_composition",
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.tla_gemm_variant.argtypes = [ctypes.POINTER(GemmArgs), ctypes.c_char_p, I32]
         L.tla_gemm_run_variant.argtypes = [ctypes.POINTER(GemmArgs), I32, P]
         L.tla_conv2d_fprop.argtypes = [ctypes.POINTER(ConvArgs), P]
+        L.tla_conv2d_fprop_variant.argtypes = [ctypes.POINTER(ConvArgs), I32, P]
         L.tla_gemm_variant_info.argtypes = [I32, I32, ctypes.POINTER(GemmKernelInfo)]
         L.tla_tiled_transpose.argtypes = [P, I64, P, I64, I64, I64, I32, P]
         L.tla_tiled_copy.argtypes = [P, I64, P, I64, I64, I64, I32, P]
@@ -186,16 +187,40 @@ class ConvArgs(ctypes.Structure):
     ]
 
 
+def conv2d_args(x, w, y, N, H, W, C, K, R, S, dtype, stride=(1, 1), pad=(0, 0), dil=(1, 1),
+                C_res=None, bias=None, bias_type=None, alpha=1.0, beta=0.0, act=ACT_NONE):
+    """The tla_conv2d_args of a convolution (see conv2d_fprop)."""
+    return ConvArgs(N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1], dil[0], dil[1],
+                    _dev(x, "x"), _dev(w, "w"), _dev(C_res, "C_res"), _dev(y, "y"), dtype,
+                    _dev(bias, "bias"), bias_type if bias_type is not None else dtype, act,
+                    alpha, beta)
+
+
 def conv2d_fprop(x, w, y, N, H, W, C, K, R, S, dtype, stride=(1, 1), pad=(0, 0), dil=(1, 1),
                  C_res=None, bias=None, bias_type=None, alpha=1.0, beta=0.0, act=ACT_NONE,
-                 stream=None):
-    """y = act(alpha * conv(x, w) + beta * C_res + bias) (tla_conv2d_fprop):
-    x NHWC, w KRSC, y and C_res NPQK, CUDA tensors of raw 16-bit storage."""
-    a = ConvArgs(N, H, W, C, K, R, S, stride[0], stride[1], pad[0], pad[1], dil[0], dil[1],
-                 _dev(x, "x"), _dev(w, "w"), _dev(C_res, "C_res"), _dev(y, "y"), dtype,
-                 _dev(bias, "bias"), bias_type if bias_type is not None else dtype, act,
-                 alpha, beta)
-    _check(lib().tla_conv2d_fprop(ctypes.byref(a), _stream(stream, x, w, y)), "tla_conv2d_fprop")
+                 stream=None, variant=None):
+    """y = act(alpha * conv(x, w) + beta * C_res + bias) (tla_conv2d_fprop, or
+    tla_conv2d_fprop_variant when `variant` is given): x NHWC, w KRSC, y and
+    C_res NPQK, CUDA tensors of raw 16-bit storage."""
+    a = conv2d_args(x, w, y, N, H, W, C, K, R, S, dtype, stride, pad, dil, C_res, bias,
+                    bias_type, alpha, beta, act)
+    s = _stream(stream, x, w, y)
+    if variant is None:
+        _check(lib().tla_conv2d_fprop(ctypes.byref(a), s), "tla_conv2d_fprop")
+    else:
+        _check(lib().tla_conv2d_fprop_variant(ctypes.byref(a), variant, s),
+               "tla_conv2d_fprop_variant")
+
+
+def conv2d_fprop_args(args: ConvArgs, stream, variant=None) -> int:
+    """Raw call with prepared ConvArgs; returns the status (no raise)."""
+    if variant is None:
+        return lib().tla_conv2d_fprop(ctypes.byref(args), stream)
+    return lib().tla_conv2d_fprop_variant(ctypes.byref(args), variant, stream)
+
+
+CONV_VARIANTS = 3
+CONV_VARIANT_NAMES = ("conv_slab", "conv_implicit_fast", "conv_implicit_general")
 
 
 GEMM_VARIANTS = 4

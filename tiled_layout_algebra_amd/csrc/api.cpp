@@ -160,19 +160,7 @@ int check_thread_map(int64_t R, int64_t C, int32_t T, int32_t V, int32_t I, int3
   return map.well_formed() ? TLA_OK : TLA_ERR_INVALID_ARG;
 }
 
-}  // namespace
-
-extern "C" {
-
-int tla_gemm_epilogue(const tla_gemm_args* args, void* stream) {
-  GemmProblem p{};
-  const int rc = validate_gemm(args, &p);
-  if (rc < 0) return rc;
-  if (rc == 1) return TLA_OK;
-  return gemm_dispatch(p, (hipStream_t)stream, false, nullptr);
-}
-
-int tla_conv2d_fprop(const tla_conv2d_args* a, void* stream) {
+int validate_conv(const tla_conv2d_args* a, ConvProblem* out) {
   if (!a) return TLA_ERR_INVALID_ARG;
   if (a->N < 0 || a->H < 1 || a->W < 1 || a->C < 1 || a->K < 1 || a->R < 1 || a->S < 1)
     return TLA_ERR_INVALID_ARG;
@@ -190,14 +178,15 @@ int tla_conv2d_fprop(const tla_conv2d_args* a, void* stream) {
   const int64_t ph = a->H + 2 * (int64_t)a->pad_h - (int64_t)a->dil_h * (a->R - 1) - 1;
   const int64_t pw = a->W + 2 * (int64_t)a->pad_w - (int64_t)a->dil_w * (a->S - 1) - 1;
   const int64_t P = ph < 0 ? 0 : ph / a->stride_h + 1, Q = pw < 0 ? 0 : pw / a->stride_w + 1;
-  if (a->N == 0 || P < 1 || Q < 1) return TLA_OK;
+  if (a->N == 0 || P < 1 || Q < 1) return 1;  // nothing to do
   if (!a->x || !a->w || !a->y) return TLA_ERR_INVALID_ARG;
   if (a->beta != 0.0f && !a->C_res) return TLA_ERR_INVALID_ARG;
   if (a->N > lim / P || a->N * P > lim / Q || a->K >= lim || a->C > lim / (a->R * a->S) ||
       a->R * a->S > lim || a->N * a->H > lim / a->W || a->N * a->H * a->W > lim / a->C)
     return TLA_ERR_INVALID_ARG;
   if (a->N * P * Q >= lim || a->R * a->S * a->C >= lim) return TLA_ERR_INVALID_ARG;
-  ConvProblem c{};
+  ConvProblem& c = *out;
+  c = ConvProblem{};
   c.N = a->N; c.H = a->H; c.W = a->W; c.C_in = a->C; c.K = a->K; c.R = a->R; c.S = a->S;
   c.P = P; c.Q = Q;
   c.u = a->stride_h; c.v = a->stride_w; c.ph = a->pad_h; c.pw = a->pad_w;
@@ -205,7 +194,36 @@ int tla_conv2d_fprop(const tla_conv2d_args* a, void* stream) {
   c.x = a->x; c.w = a->w; c.C = a->beta != 0.0f ? a->C_res : nullptr; c.y = a->y;
   c.type = a->type; c.bias = a->bias; c.bias_type = a->bias ? a->bias_type : TLA_F32;
   c.act = a->act; c.alpha = a->alpha; c.beta = a->beta;
+  return TLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tla_gemm_epilogue(const tla_gemm_args* args, void* stream) {
+  GemmProblem p{};
+  const int rc = validate_gemm(args, &p);
+  if (rc < 0) return rc;
+  if (rc == 1) return TLA_OK;
+  return gemm_dispatch(p, (hipStream_t)stream, false, nullptr);
+}
+
+int tla_conv2d_fprop(const tla_conv2d_args* a, void* stream) {
+  ConvProblem c;
+  const int rc = validate_conv(a, &c);
+  if (rc < 0) return rc;
+  if (rc == 1) return TLA_OK;
   return conv_dispatch(c, (hipStream_t)stream);
+}
+
+int tla_conv2d_fprop_variant(const tla_conv2d_args* a, int32_t variant, void* stream) {
+  if (variant < 0 || variant >= TLA_CONV_VARIANTS) return TLA_ERR_INVALID_ARG;
+  ConvProblem c;
+  const int rc = validate_conv(a, &c);
+  if (rc < 0) return rc;
+  if (rc == 1) return TLA_OK;
+  return conv_dispatch(c, (hipStream_t)stream, variant);
 }
 
 int tla_gemm_run_variant(const tla_gemm_args* args, int32_t variant, void* stream) {

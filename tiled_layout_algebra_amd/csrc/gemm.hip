@@ -509,7 +509,13 @@ const void* variant_kernel(int v, int* threads) {
 
 }  // namespace
 
-int conv_dispatch(const ConvProblem& c, hipStream_t stream) {
+// The slab convolution of conv_slab.hip for 64 input and 64 output channels
+// at stride 1 (image and filter 16-byte aligned, H*W*128 below 2^31); p is
+// the implicit-GEMM view built below.  TLA_ERR_UNSUPPORTED when no slab of
+// whole output rows fits LDS beside the filter.
+int launch_conv_slab(const GemmParams& p, int type, hipStream_t stream);
+
+int conv_dispatch(const ConvProblem& c, hipStream_t stream, int forced) {
   const int eb = elem_bytes(c.type);
   GemmParams p{};
   p.A = (const uint8_t*)c.x;
@@ -541,6 +547,19 @@ int conv_dispatch(const ConvProblem& c, hipStream_t stream) {
   const bool x_vec = (c.C_in * eb) % 16 == 0 && aligned(c.x, 16);
   const bool w_vec = ((int64_t)p.K * eb) % 16 == 0 && aligned(c.w, 16);
   p.flags |= (x_vec ? 1 << 8 : 0) | (w_vec ? 1 << 9 : 0);
+  // 64 -> 64 channels at stride 1: the image slab and the whole filter in
+  // LDS, each image element copied in once instead of once per tap (on
+  // 32 x 56 x 56 x 64 -> 64, 3x3: 14.7 us against 17.8 us for the implicit
+  // GEMM's 256 x 64 tiles).
+  if (forced <= 0) {
+    if (c.C_in == 64 && c.K == 64 && c.u == 1 && c.v == 1 && eb == 2 && aligned(c.x, 16) &&
+        aligned(c.w, 16) && c.H * c.W * 128 < (int64_t(1) << 31)) {
+      const int rc = launch_conv_slab(p, c.type, stream);
+      if (rc != TLA_ERR_UNSUPPORTED || forced == 0) return rc;
+    } else if (forced == 0) {
+      return TLA_ERR_UNSUPPORTED;
+    }
+  }
   // Direct-to-LDS implicit GEMM when every 128-byte k-tile is channels of
   // one tap (C a multiple of 64), 16-byte aligned image and filter rows and
   // both operands below 2 GiB; otherwise the register-staged loader.
@@ -556,7 +575,8 @@ int conv_dispatch(const ConvProblem& c, hipStream_t stream) {
   // 256 x 64 tile runs 8 wavefronts (4 x 2 of 64 x 32): each thread issues
   // half the copies of the 4-wavefront form, and a wave blocked on a copy
   // leaves its SIMD to the other wave's MFMAs (17.8 against 18.5 us).
-  if (fast) {
+  if (forced == 1 && !fast) return TLA_ERR_UNSUPPORTED;
+  if (fast && forced != 2) {
     const bool narrow = c.K <= 64;
     if (c.type == TLA_BF16)
       return narrow ? launch_fast<kBF16, 256, 64, 128, 2, 1, 4, 2, true>(p, stream)

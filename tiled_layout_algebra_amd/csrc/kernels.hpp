@@ -36,7 +36,10 @@ struct ConvProblem {
   int act;
   float alpha, beta;
 };
-int conv_dispatch(const ConvProblem& c, hipStream_t stream);
+// forced = -1 picks the kernel (slab, implicit direct-to-LDS, implicit
+// register-staged: the first that applies); 0..2 runs that one or returns
+// TLA_ERR_UNSUPPORTED.
+int conv_dispatch(const ConvProblem& c, hipStream_t stream, int forced = -1);
 
 // GEMM kernel variants: 0 two-group 256x256, 1 fast 128x128, 2 general
 // 128x128, 3 single-group 256x256.
