@@ -10,9 +10,9 @@ against the direct-convolution oracle on the same seeded inputs.
   output-channel and pixel counts, whole tiles through the LDS epilogue;
 * 64 -> 64 channels at stride 1 (the slab kernel: the whole filter and the
   image rows of a band of output rows in LDS) over padding, dilation,
-  R != S, 1x1, 16 taps, a last band with fewer rows, and the shapes that
-  fall back to the implicit GEMM (5x5: the filter does not fit beside a
-  slab; rows wider than 512 pixels);
+  R != S, 1x1, 16 taps, bands of several rows with a last band of fewer,
+  and the shapes that fall back to the implicit GEMM (5x5: the filter does
+  not fit beside a slab; rows wider than 512 pixels);
 * every kernel forced through tla_conv2d_fprop_variant on a subset, bit for
   bit where it applies and refused where it does not;
 * random inputs with GELU within the tolerance, C aliasing y;
@@ -88,6 +88,8 @@ GEOMETRIES = [  # N, H, W, C, K, R, S, stride, pad, dil
     # 3x5 and 4x4 filters (16 taps: 128 KiB of filter beside the slab)
     (10, 27, 27, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
     (40, 14, 14, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
+    # more than 256 bands of one row: bands of several rows, the last shorter
+    (24, 48, 48, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
     (2, 7, 9, 64, 64, 3, 5, (1, 1), (1, 2), (1, 1)),
     (1, 6, 9, 64, 64, 4, 4, (1, 1), (3, 3), (2, 1)),
     # coordinates near 2^20 (padding, stride and dilation): taps on both sides

@@ -252,7 +252,9 @@ __global__ __launch_bounds__(64 * kWaves) void conv_slab_kernel(const GemmParams
   // ---- epilogue of the wave's tile.  Once every wave is done with the slab
   // and the filter, each wave stages its tile's C and y through its own
   // LDS region, so both move as whole rows; rows past the workgroup's valid
-  // pixels are left alone.
+  // pixels are left alone.  (The release fence keeps every slab and filter
+  // read of this wave above the barrier: the regions overlap them.)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   stage_barrier();
   if (!busy) return;
   GemmParams e = p;
