@@ -208,3 +208,32 @@ def test_wide_layer_sampled():
                            beta=case.beta, act=case.act)
     ok, worst = og.within_tolerance(og.decode(case.dtype, got[ms, ks]), ref, case.tol)
     assert ok, "worst |y-ref|/(1+|ref|) = %g" % worst
+
+
+@pytest.mark.parametrize("variant", [0, 1])
+def test_64_channels_fp32_bias_and_c(variant):
+    """An fp32 bias (not y's type) sends the slab kernel's and the implicit
+    GEMM's epilogues down the per-element path; integer inputs, bit-exact,
+    with C and a band whose last tile is partial."""
+    case = W.ConvCase(name="f32bias", N=3, H=9, W=10, C=64, K=64, R=3, S=3, pad=(1, 1),
+                      dtype=W.F16, alpha=0.5, beta=1.5, act=W.ACT_RELU, has_c=True,
+                      has_bias=False, seed=41, dist="int3")
+    inp = W.conv_inputs(case)
+    rng = np.random.default_rng(42)
+    inp["bias"] = W.encode(rng.integers(-8, 9, size=case.K) / 8.0, W.F32)
+    P, Q = case.out_hw()
+    x, w, c = to_dev(inp["x"]), to_dev(inp["w"]), to_dev(inp["C"])
+    b = to_dev(inp["bias"])
+    y = torch.full((case.N * P * Q * case.K,), 0x5A5A, dtype=torch.int16, device="cuda")
+    tla.conv2d_fprop(x, w, y, case.N, case.H, case.W, case.C, case.K, case.R, case.S,
+                     case.dtype, case.stride, case.pad, case.dil, C_res=c, bias=b,
+                     bias_type=W.F32, alpha=case.alpha, beta=case.beta, act=case.act,
+                     variant=variant)
+    torch.cuda.synchronize()
+    got = to_host(y, np.dtype(np.uint16)).reshape(case.N * P * Q, case.K)
+    ref = oc.conv2d(inp["x"], inp["w"], case.N, case.H, case.W, case.C, case.K, case.R, case.S,
+                    case.stride, case.pad, case.dil, case.dtype, Cres=inp["C"], bias=inp["bias"],
+                    bias_type=W.F32, alpha=case.alpha, beta=case.beta, act=case.act)
+    want = W.encode(ref, case.dtype).reshape(got.shape)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "v%d: %d mismatches, first at %s" % (variant, len(bad), bad[0])
