@@ -127,19 +127,25 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  *                            between MFMA-only and memory phases; direct
  *                            global->LDS copies; every operand type
  *   1 "gemm_fast_128x128"    128x128 tiles, direct copies (16-bit: 8
- *                            wavefronts of 64x32; e4m3: 4 of 64x64)
+ *                            wavefronts of 64x32; e4m3: 4 of 64x64); for
+ *                            16-bit operands B may also be N-contiguous
+ *                            (row-major K x N): its fragments are then read
+ *                            through LDS transpose reads
  *   2 "gemm_general_128x128" 128x128 tiles, 4 wavefronts, register-staged
  *                            predicated loads: any order, pitch, alignment,
  *                            ragged K
  *   3 "gemm_fast_256x256"    256x256 tiles, one group (16-bit: 8 wavefronts
  *                            of 128x64; e4m3: 4 of 128x128), direct copies
  * tla_gemm_epilogue picks one from the problem: in the fast layout,
- * variant 0 with at least 128 tiles of 256x256 and 1 otherwise; variant 2
- * outside it;
+ * variant 0 with at least 128 tiles of 256x256 and 1 otherwise; variant 1
+ * in the N-contiguous-B layout; variant 2 outside both;
  * tla_gemm_run_variant runs the one asked for, with the same semantics and
  * tolerance, or returns TLA_ERR_UNSUPPORTED when a fast variant is asked
  * for a problem without the fast layout (both operands K-contiguous,
- * 16-byte aligned rows, K a multiple of 128 bytes, each operand < 2 GiB).
+ * 16-byte aligned rows, K a multiple of 128 bytes, each operand < 2 GiB) --
+ * variant 1 also accepts the N-contiguous-B layout (16-bit operands; A as
+ * in the fast layout; B row-major with 16-byte aligned rows, N a multiple
+ * of 8, K a multiple of 64, B below 2 GiB).
  * Variant ids outside [0, TLA_GEMM_VARIANTS) are TLA_ERR_INVALID_ARG.
  */
 #define TLA_GEMM_VARIANTS 4

@@ -56,8 +56,20 @@ namespace {
 // plus an immediate (slot and tile row).  The XOR swizzle only sees row bits
 // below 32, so one base per k-step serves every 32-row fragment; grouping
 // the A slots and the B slots keeps every immediate below 64 KiB.
+//
+// kBT: B is N-contiguous (a row-major K x N matrix, 16-bit).  Its slab is
+// BK rows of k, each BN columns of n (2*BN bytes, 16-byte chunk c of row r
+// stored at chunk c ^ 4 (r % 4)), filled by the same direct copies; a B
+// fragment (32 columns n x 16 k, lane l: column l % 32, k 8 (l / 32) .. + 7)
+// is two ds_read_b64_tr_b16, each giving a lane four consecutive k of its
+// column.  In a quarter-wave the instruction hands lane j element e from
+// the 8 bytes addressed by lane 4 e + j / 4, at position j % 4; so lane a
+// of the quarter-wave addresses row k0 + a / 4, columns n0 + 4 (a % 4) ..
+// + 3, and lane j receives B[k0 .. k0 + 3][n0 + j].  The swizzle keeps the
+// 32 lanes of one half-wave (rows k0 .. k0 + 3, 32 bytes each of two
+// column groups) on 16 distinct 16-byte bank groups.
 template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront = 0, int kWM = 2,
-          int kWN = 2, bool kConv = false>
+          int kWN = 2, bool kConv = false, bool kBT = false>
 __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmParams p) {
   using Atom = MfmaAtom<kCode>;
   using Frag = typename Atom::Frag;
@@ -74,6 +86,10 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
   constexpr int SLAB_A = BM * kRowBytes, SLAB_B = BN * kRowBytes;
   constexpr int B_BASE = kStages * SLAB_A;
   static_assert(kStages * (SLAB_A + SLAB_B) <= 160 * 1024, "LDS budget");
+  static_assert(!kBT || (EB == 2 && BN >= 128 && !kConv && kWN * 32 == BN),
+                "N-contiguous B: 16-bit, one 32-column fragment per wave");
+  constexpr int kRowBT = BN * 2;                   // bytes per k row of an N-contiguous slab
+  constexpr int kChBT = kRowBT / 16;
   static_assert(kStages * SLAB_A <= 65536 && kStages * SLAB_B <= 65536, "fragment immediates");
   constexpr int kChunks = Slab<kRowBytes>::kChunks;
   static_assert((1 << Slab<kRowBytes>::kRowShift) * kChunks <= 32, "swizzle period divides 32 rows");
@@ -81,7 +97,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
   static_assert(IA * NT == BM * kChunks && IB * NT == BN * kChunks, "whole copy instructions");
   constexpr int kLoads = IA + IB;                  // copies per thread per tile
   constexpr int kSub = Atom::kLaneBytes / 16;      // 16-byte reads per fragment
-  constexpr int kReads = (FM + FN) * kSub;
+  constexpr int kReads = FM * kSub + (kBT ? 2 : FN * kSub);
   constexpr int kMfmas = FM * FN;
   constexpr int kStepBytes = Atom::kK * EB;
   // Copies per full step, the rest go into the first half of the last step.
@@ -109,10 +125,19 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
   static_for<kLoads>([&](auto q) {
     constexpr bool kA = q < IA;
     constexpr int qq = kA ? q : q - IA;
-    const int r = tid / kChunks + (NT / kChunks) * qq;
-    const int64_t row = kA ? min(m0 + r, p.M - 1) : min(n0 + r, p.N - 1);
-    const int64_t rb = (kA ? p.a_sr : p.b_sr) * EB;
-    off[q] = (uint32_t)(row * rb + Swz::chunk(r, tid % kChunks) * 16);
+    if constexpr (!kA && kBT) {
+      // slab chunk tid + NT q': k row r, stored chunk pc, which holds logical
+      // chunk pc ^ 4 (r % 4): columns n0 + 8 lc .. + 7, clamped to the last
+      // whole chunk of the matrix (columns past N are never stored)
+      const int sc = tid + NT * qq, r = sc / kChBT, pc = sc % kChBT;
+      const int n = min(n0 + 8 * (pc ^ (4 * (r & 3))), p.N - 8);
+      off[q] = (uint32_t)(((int64_t)r * p.b_sk + n) * EB);
+    } else {
+      const int r = tid / kChunks + (NT / kChunks) * qq;
+      const int64_t row = kA ? min(m0 + r, p.M - 1) : min(n0 + r, p.N - 1);
+      const int64_t rb = (kA ? p.a_sr : p.b_sr) * EB;
+      off[q] = (uint32_t)(row * rb + Swz::chunk(r, tid % kChunks) * 16);
+    }
   });
   // Implicit-GEMM convolution: A row m is the output pixel (n, p, q); a
   // k-tile is 128 bytes of channels of one filter tap (C is a multiple of
@@ -146,6 +171,20 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
       fb[ks][u] = (uint32_t)(B_BASE + rb * kRowBytes + Swz::chunk(rb, c) * 16);
     });
   });
+  // N-contiguous B: the two transpose reads of k-step ks (k0 = 16 ks +
+  // 8 (quarter-wave / 2) + 4 h) for lane a = lane % 16 of its quarter-wave
+  uint32_t fbt[kBT ? KSTEPS : 1][2];
+  if constexpr (kBT) {
+    const int qw = lane >> 4, a4 = lane & 15;
+    static_for<KSTEPS>([&](auto ks) {
+      static_for<2>([&](auto h) {
+        const int k = 16 * ks + 8 * (qw >> 1) + 4 * h + (a4 >> 2);
+        const int n = wn0 + 16 * (qw & 1) + 4 * (a4 & 3);
+        fbt[ks][h] = (uint32_t)(B_BASE + k * kRowBT + (((n >> 3) ^ (4 * (k & 3))) * 16) +
+                                (n & 7) * 2);
+      });
+    });
+  }
 
   f32x16 acc[FM][FN];
   static_for<FM>([&](auto i) { static_for<FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
@@ -159,9 +198,21 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
       return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
+  auto lds_frag_t = [&](const uint32_t (&base)[2], int imm) -> Frag {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef int s32x2 __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + base[0] + imm));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + base[1] + imm));
+    const s32x2 l2 = __builtin_bit_cast(s32x2, lo), h2 = __builtin_bit_cast(s32x2, hi);
+    return Frag{l2[0], l2[1], h2[0], h2[1]};
+  };
   auto read_frags = [&](auto buf, auto slot, auto ks) {
     static_for<FM>([&](auto i) { a[buf][i] = lds_frag(fa[ks], slot * SLAB_A + i * 32 * kRowBytes); });
-    static_for<FN>([&](auto j) { b[buf][j] = lds_frag(fb[ks], slot * SLAB_B + j * 32 * kRowBytes); });
+    if constexpr (kBT)
+      b[buf][0] = lds_frag_t(fbt[ks], slot * SLAB_B);
+    else
+      static_for<FN>([&](auto j) { b[buf][j] = lds_frag(fb[ks], slot * SLAB_B + j * 32 * kRowBytes); });
   };
   auto mma = [&](auto buf, auto idx) {
     Atom::mma(acc[idx / FN][idx % FN], b[buf][idx % FN], a[buf][idx / FN]);
@@ -184,6 +235,9 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
                 smem + slot * SLAB_A + (wave * 64 + NT * q) * 16, x_records);
     } else if constexpr (q < IA)
       dma16_buf(p.A, off[q], kb, smem + slot * SLAB_A + (wave * 64 + NT * q) * 16);
+    else if constexpr (kBT)
+      dma16_buf(p.B, off[q], (uint32_t)(min(t, KT - 1) * BK) * (uint32_t)(p.b_sk * EB),
+                smem + B_BASE + slot * SLAB_B + (wave * 64 + NT * (q - IA)) * 16);
     else
       dma16_buf(p.B, off[q], kb, smem + B_BASE + slot * SLAB_B + (wave * 64 + NT * (q - IA)) * 16);
   };
@@ -420,14 +474,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
 
 // ----------------------------------------------------------------- dispatch
 template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront, int kWM, int kWN,
-          bool kConv = false>
+          bool kConv = false, bool kBT = false>
 int launch_fast(const GemmParams& p0, hipStream_t stream) {
   GemmParams p = p0;
   int64_t grid;
   set_grid(p, BM, BN, &grid);
   if (grid <= 0) return TLA_OK;
   if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((gemm_fast_kernel<kCode, BM, BN, kRowBytes, kStages, kFront, kWM, kWN, kConv>),
+  hipLaunchKernelGGL((gemm_fast_kernel<kCode, BM, BN, kRowBytes, kStages, kFront, kWM, kWN, kConv,
+                                       kBT>),
                      dim3((unsigned)grid), dim3(64 * kWM * kWN), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
 }
@@ -463,13 +518,20 @@ const char* const kVariantNames[kGemmVariants] = {"gemm_pingpong_256x256", "gemm
                                                   "gemm_general_128x128", "gemm_fast_256x256"};
 const int kVariantTile[kGemmVariants] = {256, 128, 128, 256};
 
+// `bt`: not the fast layout, but A is and B is N-contiguous (16-bit, whole
+// 16-byte chunks of n): variant 1's kernel takes B through LDS transpose
+// reads.
 template <int kCode>
-int dispatch_typed(const GemmParams& p, bool fast, bool big, hipStream_t s, bool dry,
+int dispatch_typed(const GemmParams& p, bool fast, bool bt, bool big, hipStream_t s, bool dry,
                    const char** name, int forced) {
-  const int v = forced >= 0 ? forced : (fast ? (big ? 0 : 1) : 2);
-  if (v != 2 && !fast) return TLA_ERR_UNSUPPORTED;  // a fast variant needs the fast layout
+  const int v = forced >= 0 ? forced : (fast ? (big ? 0 : 1) : (bt ? 1 : 2));
+  // a fast variant needs the fast layout (variant 1 also takes `bt`)
+  if (v != 2 && !fast && !(v == 1 && bt)) return TLA_ERR_UNSUPPORTED;
   if (name) *name = kVariantNames[v];
   if (dry) return TLA_OK;
+  if constexpr (kCode != kE4M3) {
+    if (v == 1 && !fast) return launch_fast<kCode, 128, 128, 128, 3, 1, 2, 4, false, true>(p, s);
+  }
   if (v == 0) return launch_pingpong(p, kCode, s);
   if constexpr (kCode == kE4M3) {
     if (v == 3) return launch_two_stage<kCode, 256, 256, 128, true>(p, s);
@@ -664,12 +726,18 @@ int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const 
   const bool small_ops = (int64_t)g.M * g.lda * eb < (int64_t(1) << 31) &&
                          (int64_t)g.N * g.ldb * eb < (int64_t(1) << 31);
   const bool fast = a_vec && b_vec && small_ops && g.K > 0 && (g.K % BK) == 0;
+  // A in the fast layout, B a 16-bit row-major K x N matrix with 16-byte
+  // aligned rows and whole 16-byte chunks of columns, below 2 GiB
+  const bool bt = !fast && eb == 2 && a_vec && g.b_order == TLA_ROW_MAJOR &&
+                  ((g.ldb * eb) % 16) == 0 && aligned(g.B, 16) && g.N % 8 == 0 &&
+                  (int64_t)g.M * g.lda * eb < (int64_t(1) << 31) &&
+                  (int64_t)g.K * g.ldb * eb < (int64_t(1) << 31) && g.K > 0 && (g.K % BK) == 0;
   const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256);
   const bool big = tiles256 >= 128;
   switch (g.a_type) {
-    case TLA_BF16: return dispatch_typed<kBF16>(p, fast, big, stream, dry_run, name, forced);
-    case TLA_F16: return dispatch_typed<kF16>(p, fast, big, stream, dry_run, name, forced);
-    case TLA_E4M3: return dispatch_typed<kE4M3>(p, fast, big, stream, dry_run, name, forced);
+    case TLA_BF16: return dispatch_typed<kBF16>(p, fast, bt, big, stream, dry_run, name, forced);
+    case TLA_F16: return dispatch_typed<kF16>(p, fast, bt, big, stream, dry_run, name, forced);
+    case TLA_E4M3: return dispatch_typed<kE4M3>(p, fast, false, big, stream, dry_run, name, forced);
     default: return TLA_ERR_UNSUPPORTED;
   }
 }
