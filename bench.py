@@ -115,6 +115,37 @@ def sweep(steps, warmup):
                                  "←" if info["name"] == auto else ""))
                 print(lines[-1], file=sys.stderr, flush=True)
             del dA, dB, dD
+    # bf16 with a row-major (N-contiguous) B: the variants that accept it
+    lines += ["", "| B row-major (bf16) | variant | M×N×K | µs | TFLOP/s | % peak | auto |",
+              "|---|---|---|---|---|---|---|"]
+    for M, N, K in SWEEP_SHAPES:
+        case = W.GemmCase(name="sweep_nn", M=M, N=N, K=K, a_type=W.BF16, b_type=W.BF16,
+                          d_type=W.BF16, b_order=W.ROW, seed=7)
+        inp = W.gemm_inputs(case)
+        dA, dB = to_dev(inp["A"]), to_dev(inp["B"])
+        dD = torch.empty(M * N, dtype=torch.int16, device="cuda")
+        call = (M, N, K, dA, W.BF16, case.a_order, case.lda, dB, W.BF16, case.b_order,
+                case.ldb, dD, W.BF16, case.d_order, case.ldd)
+        auto = tla.gemm_variant(*call)
+        for v in (1, 2):
+            def run():
+                tla.gemm_epilogue(*call, stream=stream.cuda_stream, variant=v)
+            for _ in range(warmup):
+                run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(steps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+            name = tla.gemm_variant_info(v, W.BF16)["name"]
+            lines.append("| bf16 NN | %s | %d×%d×%d | %.1f | %.0f | %.1f | %s |" % (
+                name, M, N, K, us, tf, 100 * tf / PEAK_BF16_TFLOPS, "←" if name == auto else ""))
+            print(lines[-1], file=sys.stderr, flush=True)
+        del dA, dB, dD
     # convolution: every kernel that applies, forced through
     # tla_conv2d_fprop_variant with prepared arguments (a launch costs the
     # host a few microseconds, less than any of these kernels)

@@ -125,7 +125,9 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  *   0 "gemm_pingpong_256x256" 256x256 tiles, 8 wavefronts in two groups of
  *                            four (2x2 waves of 64x128 each) that take turns
  *                            between MFMA-only and memory phases; direct
- *                            global->LDS copies; every operand type
+ *                            global->LDS copies; every operand type (16-bit
+ *                            operands may also have an N-contiguous B, as
+ *                            for variant 1)
  *   1 "gemm_fast_128x128"    128x128 tiles, direct copies (16-bit: 8
  *                            wavefronts of 64x32; e4m3: 4 of 64x64); for
  *                            16-bit operands B may also be N-contiguous
@@ -143,9 +145,9 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  * tolerance, or returns TLA_ERR_UNSUPPORTED when a fast variant is asked
  * for a problem without the fast layout (both operands K-contiguous,
  * 16-byte aligned rows, K a multiple of 128 bytes, each operand < 2 GiB) --
- * variant 1 also accepts the N-contiguous-B layout (16-bit operands; A as
- * in the fast layout; B row-major with 16-byte aligned rows, N a multiple
- * of 8, K a multiple of 64, B below 2 GiB).
+ * variants 0 and 1 also accept the N-contiguous-B layout (16-bit operands;
+ * A as in the fast layout; B row-major with 16-byte aligned rows, N a
+ * multiple of 8, K a multiple of 64, B below 2 GiB).
  * Variant ids outside [0, TLA_GEMM_VARIANTS) are TLA_ERR_INVALID_ARG.
  */
 #define TLA_GEMM_VARIANTS 4

@@ -99,8 +99,17 @@ def test_gemm_variant_choice():
     assert _variant(_args(**dict(e4, M=1024, N=1024)))[1] == "gemm_fast_128x128"
     # fp8 slabs are 128 elements wide: K = 64 is ragged for e4m3
     assert _variant(_args(**dict(e4, K=64, lda=64, ldb=64)))[1] == "gemm_general_128x128"
-    # N-contiguous B, odd pitches, misaligned bases, ragged K: general
-    assert _variant(_args(b_order=tla.ROW_MAJOR))[1] == "gemm_general_128x128"
+    # N-contiguous 16-bit B with aligned rows: the 128 x 128 transpose-read
+    # kernel at every size
+    assert _variant(_args(b_order=tla.ROW_MAJOR))[1] == "gemm_fast_128x128"
+    big_nn = dict(M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldd=4096, b_order=tla.ROW_MAJOR)
+    assert _variant(_args(**big_nn))[1] == "gemm_fast_128x128"
+    # ... but not for e4m3, N not a multiple of 8, unaligned B rows or ragged K
+    assert _variant(_args(**dict(e4, b_order=tla.ROW_MAJOR)))[1] == "gemm_general_128x128"
+    assert _variant(_args(b_order=tla.ROW_MAJOR, N=60, ldd=60, ldb=60))[1] == "gemm_general_128x128"
+    assert _variant(_args(b_order=tla.ROW_MAJOR, ldb=67))[1] == "gemm_general_128x128"
+    assert _variant(_args(b_order=tla.ROW_MAJOR, K=96, lda=96))[1] == "gemm_general_128x128"
+    # odd pitches, misaligned bases, ragged K: general
     assert _variant(_args(lda=65))[1] == "gemm_general_128x128"
     assert _variant(_args(A=FAKE + 2))[1] == "gemm_general_128x128"
     assert _variant(_args(K=63, lda=64, ldb=64))[1] == "gemm_general_128x128"
@@ -224,9 +233,12 @@ def test_run_variant_argument_errors():
     a = _args()
     for bad in (-1, tla.GEMM_VARIANTS, 99):
         assert tla.lib().tla_gemm_run_variant(ctypes.byref(a), bad, None) == tla.ERR_INVALID_ARG
-    nn = _args(b_order=tla.ROW_MAJOR, ldb=64)
+    nn = _args(b_order=tla.ROW_MAJOR, ldb=67)   # B rows not 16-byte aligned
     for v in (0, 1, 3):
         assert tla.lib().tla_gemm_run_variant(ctypes.byref(nn), v, None) == tla.ERR_UNSUPPORTED
+    # aligned N-contiguous B: the single-group 256 x 256 kernel has no such form
+    nn = _args(b_order=tla.ROW_MAJOR, ldb=64)
+    assert tla.lib().tla_gemm_run_variant(ctypes.byref(nn), 3, None) == tla.ERR_UNSUPPORTED
 
 
 def _conv(**kw):

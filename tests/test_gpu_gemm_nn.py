@@ -1,14 +1,16 @@
 """GEMM parity with an N-contiguous B (a row-major K x N matrix) on the fast
-128 x 128 kernel, whose B fragments come through LDS transpose reads
-(ds_read_b64_tr_b16), through the C ABI against the oracle:
+128 x 128 kernel and the two-group 256 x 256 kernel, whose B fragments come
+through LDS transpose reads (ds_read_b64_tr_b16), through the C ABI against
+the oracle:
 
 * integer-valued inputs, bit for bit, over both 16-bit types, the whole
   epilogue (alpha, beta*C, bias, ReLU), ragged M and N (N a multiple of 8,
   down to one 16-byte chunk), K from one k-tile up, and pitched operands
   with NaN padding;
-* the kernel choice: variant 1 by default, variants 0 and 3 refused, the
-  general kernel still forcible;
-* random inputs at 2048 x 2048 x 1024 within the tolerance.
+* the kernel choice: variant 1 at every size, variant 0 forcible (its own
+  transpose-read form), variant 3 refused, the general kernel forcible;
+* random inputs at 2048 x 2048 x 1024 and 4096 x 4096 x 512 within the
+  tolerance.
 Tolerance: |D - ref| <= tol*(1 + |ref|), tol 1e-2.
 """
 import numpy as np
@@ -69,14 +71,33 @@ def test_row_major_b_unaligned_pitch_takes_general_path():
     _exact(case, W.gemm_inputs(case))
 
 
-def test_row_major_b_forced_variants():
-    case = _case(300, 520, 384, W.BF16, seed=7)
+@pytest.mark.parametrize("a_type", [W.F16, W.BF16])
+def test_row_major_b_forced_variants(a_type):
+    case = _case(300, 520, 384, a_type, seed=7)
     inp = W.gemm_inputs(case)
-    for v in (1, 2):
+    for v in (0, 1, 2):
         _exact(case, inp, variant=v)
-    for v in (0, 3):
-        with pytest.raises(tla.TlaError, match="UNSUPPORTED"):
-            G.run_gemm(case, inp, sentinel=SENT, variant=v)
+    with pytest.raises(tla.TlaError, match="UNSUPPORTED"):
+        G.run_gemm(case, inp, sentinel=SENT, variant=3)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (513, 776, 320), (1000, 1032, 1024)])
+def test_row_major_b_two_group_kernel_bit_exact(M, N, K):
+    case = _case(M, N, K, W.BF16, seed=M + N + K)
+    _exact(case, W.gemm_inputs(case), variant=0)
+
+
+def test_row_major_b_random_4096_two_group_kernel():
+    case = W.GemmCase(name="nn_rand_big", M=4096, N=4096, K=512, a_type=W.BF16, b_type=W.BF16,
+                      d_type=W.BF16, a_order=W.ROW, b_order=W.ROW, alpha=1.5, beta=0.5,
+                      act=W.ACT_RELU, has_c=True, has_bias=True, seed=9)
+    assert G.variant(case) == "gemm_fast_128x128"
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT, variant=0)
+    assert G.padding_untouched(case, D, SENT)
+    got = og.decode(case.d_type, W.d_logical(case, D).copy())
+    ok, worst = og.within_tolerance(got, G.oracle_ref(case, inp), case.tol)
+    assert ok, "worst |D-ref|/(1+|ref|) = %g" % worst
 
 
 def test_row_major_b_random_2048():

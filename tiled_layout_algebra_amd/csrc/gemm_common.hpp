@@ -46,8 +46,10 @@ struct GemmParams {
 
 // The two-group 256 x 256 kernel of gemm_pingpong.hip for 16-bit or e4m3
 // operands in the fast layout (both operands K-contiguous with 16-byte
-// aligned rows, K a multiple of 128 bytes, each operand below 2 GiB).
-int launch_pingpong(const GemmParams& p, int a_type, hipStream_t stream);
+// aligned rows, K a multiple of 128 bytes, each operand below 2 GiB); with
+// `bt`, 16-bit operands whose B is N-contiguous instead (16-byte aligned
+// rows, N a multiple of 8).
+int launch_pingpong(const GemmParams& p, int a_type, hipStream_t stream, bool bt = false);
 const void* pingpong_kernel(int a_type);
 
 namespace {
@@ -87,6 +89,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// ds_read_b64_tr_b16: four 16-bit elements per lane, transposed across each
+// quarter-wave (lane j gets element j % 4 of the 8 bytes addressed by lanes
+// 4 e + j / 4, e = 0..3).  The restrict-qualified parameter gives the read
+// its own alias scope: without one the compiler makes the read wait for
+// every direct HBM -> LDS copy in flight (vmcnt(0)), as it does not for
+// plain LDS reads; the kernels order their copies and reads with explicit
+// waits and barriers either way.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 ds_read_tr16(const uint8_t* __restrict__ p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
 
 __device__ __forceinline__ lds_void_t* to_lds(void* p) { return (lds_void_t*)(p); }
 

@@ -33,12 +33,24 @@
 // real row, so a lane whose row lies past M (or N) reads zeros and touches
 // no memory; the per-lane offset (row r0, swizzled chunk) is the same for
 // every copy and every k-tile, and the k-tile's byte offset is a scalar.
+//
+// kBT: B is N-contiguous (a row-major K x N matrix, 16-bit).  Its slab holds
+// the k-tile's 64 rows of k, each the tile's 256 columns of n (512 bytes,
+// 16-byte chunk c of row r stored at chunk c ^ 4 (r % 4)); copy q moves rows
+// 8q .. 8q + 7 (the scalar offset carries the row), and columns past N read
+// the last whole chunk of the row (never stored).  A B fragment is two
+// ds_read_b64_tr_b16 (quarter-wave lane j receives element e from the
+// 8 bytes lane 4 e + j / 4 addresses, at position j % 4), so lane a of a
+// quarter-wave addresses row k0 + a / 4, columns n0 + 4 (a % 4) .. and lane
+// j gets B[k0 .. k0 + 3][n0 + j].  The swizzle term 4 (r % 4) sits in
+// address bits 6-7, which hold nothing else, so the wave's four 32-column
+// fragments are one base XOR 64 j.
 #include "gemm_common.hpp"
 
 namespace tla {
 namespace {
 
-template <int kCode>
+template <int kCode, bool kBT = false>
 __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) {
   using Atom = MfmaAtom<kCode>;
   using Frag = typename Atom::Frag;
@@ -60,6 +72,7 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   static_assert((1 << Slab<kRowBytes>::kRowShift) * kChunks <= 32,
                 "the swizzle repeats within 32 rows");
   static_assert(5 * SLAB <= 160 * 1024, "LDS budget");
+  static_assert(!kBT || EB == 2, "N-contiguous B: 16-bit operands");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * SLAB];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -81,22 +94,42 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   const int64_t rb = (grp == 0 ? p.a_sr : p.b_sr) * EB;   // row pitch in bytes
   const uint8_t* op = (grp == 0 ? p.A + m0 * rb : p.B + n0 * rb);  // the tile's first row
   const int rows_left = (grp == 0 ? p.M - m0 : p.N - n0); // real rows from there on
-  const uint32_t voff = (uint32_t)(r0 * rb + Swz::chunk(r0, t % kChunks) * 16);
+  uint32_t voff = (uint32_t)(r0 * rb + Swz::chunk(r0, t % kChunks) * 16);
   const int lds_op = grp == 0 ? 0 : B_BASE;
   int recs[kCopies];
   static_for<kCopies>([&](auto q) {
     recs[q] = (int)(min(max(rows_left - 32 * (int)q, 0), 32) * rb);
   });
+  // per group: the byte step of a k-tile, and (N-contiguous B) of a copy
+  uint32_t kt_bytes = kRowBytes, q_bytes = 0;
+  const uint8_t* qbase = op;
+  int64_t q_stride = 32 * rb;
+  if constexpr (kBT) {
+    if (grp == 1) {
+      // slab chunk t + 256 q: row r0 = t / 32 (+ 8 q), stored chunk t % 32
+      // holding columns n0 + 8 ((t % 32) ^ 4 (r0 % 4)) .. + 7
+      const int64_t ldb = p.b_sk;
+      const int rt = t >> 5;
+      const int n = min(n0 + 8 * ((t & 31) ^ (4 * (rt & 3))), p.N - 8);
+      voff = (uint32_t)((rt * ldb + n) * EB);
+      kt_bytes = (uint32_t)(BK * ldb * EB);
+      q_bytes = (uint32_t)(8 * ldb * EB);
+      qbase = p.B;
+      q_stride = 0;
+      const int64_t whole = (int64_t)p.K * ldb * EB;
+      static_for<kCopies>([&](auto q) { recs[q] = (int)min(whole, (int64_t)0x7FFFFFFF); });
+    }
+  }
   // Copy q of k-tile kt into `slot`.  A copy past the last k-tile still runs
   // (so the instruction stream and the wait counts never change) but with no
   // records: it writes zeros into a slot nobody reads any more.
   auto copy_one = [&](int kt, int slot, bool live, auto q) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(op + (int64_t)(32 * q) * rb), 0, recs[q] & -(int)live, 0x00020000);
+        (void*)(qbase + (int64_t)q * q_stride), 0, recs[q] & -(int)live, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(smem + lds_op + slot * SLAB + q * 4096 +
                                                      (wave & 3) * 1024),
-        16, voff, (uint32_t)kt * kRowBytes, 0, 0);
+        16, voff, (uint32_t)kt * kt_bytes + (uint32_t)q * q_bytes, 0, 0);
   };
   auto copy_slab = [&](int kt, int slot, bool live) {
     static_for<kCopies>([&](auto q) { copy_one(kt, slot, live, q); });
@@ -110,13 +143,26 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   // one's address XOR 16 (every other term of the address is a multiple of
   // 128), formed in the loop rather than held.
   static_assert(kSub == 1 || (Atom::kLaneBytes == 32 && kStepBytes % 32 == 0), "chunk pairs");
-  uint32_t fa[KSTEPS], fb[KSTEPS];
+  uint32_t fa[KSTEPS], fb[kBT ? 1 : KSTEPS];
   static_for<KSTEPS>([&](auto ks) {
     const int c = (ks * kStepBytes + (lane >> 5) * Atom::kLaneBytes) / 16;
     const int ra = wm0 + (lane & 31), rbw = wn0 + (lane & 31);
     fa[ks] = (uint32_t)(ra * kRowBytes + Swz::chunk(ra, c) * 16);
-    fb[ks] = (uint32_t)(B_BASE + rbw * kRowBytes + Swz::chunk(rbw, c) * 16);  // B slot 0
+    if constexpr (!kBT)
+      fb[ks] = (uint32_t)(B_BASE + rbw * kRowBytes + Swz::chunk(rbw, c) * 16);  // B slot 0
   });
+  if constexpr (kBT) {
+    // transpose read h of k-step ks for lane a of quarter-wave qw: row
+    // k = 16 ks + 8 (qw / 2) + 4 h + a / 4, columns n = wn0 + 16 (qw % 2) +
+    // 4 (a % 4) of the first 32-column fragment, stored chunk
+    // (n / 8) ^ 4 (k % 4).  k % 4 = a / 4 whatever ks and h, so one base
+    // (ks = h = 0) serves all: + 8192 ks + 2048 h, and XOR 64 j for
+    // fragment j
+    const int qw = lane >> 4, a4 = lane & 15;
+    const int k = 8 * (qw >> 1) + (a4 >> 2);
+    const int n = wn0 + 16 * (qw & 1) + 4 * (a4 & 3);
+    fb[0] = (uint32_t)(B_BASE + k * 512 + (((n >> 3) ^ (4 * (k & 3))) * 16) + (n & 7) * 2);
+  }
   Frag a[KSTEPS][FM], b[KSTEPS][FN];
   auto lds_frag = [&](uint32_t base, int imm) -> Frag {
     if constexpr (kSub == 1) {
@@ -131,16 +177,25 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   };
   // k-tile kt: A slot kt % 2 (immediate), B slot kt % 3 (in fb); afterwards
   // fb moves on to B slot (kt + 1) % 3
+  auto lds_frag_t = [&](uint32_t addr) -> Frag {
+    typedef int s32x2 __attribute__((ext_vector_type(2)));
+    const s16x4 lo = ds_read_tr16(smem + addr);
+    const s16x4 hi = ds_read_tr16(smem + addr + 2048);
+    const s32x2 l2 = __builtin_bit_cast(s32x2, lo), h2 = __builtin_bit_cast(s32x2, hi);
+    return Frag{l2[0], l2[1], h2[0], h2[1]};
+  };
   auto read_frag = [&](int kt, auto r) {
     constexpr int ks = r / (FM + FN), f = r % (FM + FN);
     if constexpr (f < FM)
       a[ks][f] = lds_frag(fa[ks], (kt & 1) * SLAB + f * 32 * kRowBytes);
+    else if constexpr (kBT)
+      b[ks][f - FM] = lds_frag_t((fb[0] ^ (64u * (f - FM))) + 8192 * ks);
     else
       b[ks][f - FM] = lds_frag(fb[ks], (f - FM) * 32 * kRowBytes);
   };
   auto advance_b = [&](int kt) {
     const int step = (kt % 3 == 2) ? -2 * SLAB : SLAB;
-    static_for<KSTEPS>([&](auto ks) { fb[ks] += step; });
+    static_for<kBT ? 1 : KSTEPS>([&](auto ks) { fb[ks] += step; });
   };
   // A memory phase: read k-tile kt's fragments and copy k-tile ct into
   // `slot`.  Under load the copy path accepts a direct-to-LDS copy only every
@@ -153,6 +208,12 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   // 4276 (copies first) for e4m3.
   constexpr int kReads = KSTEPS * (FM + FN);  // fragments per k-tile
   constexpr int kPer = kReads / kCopies, kRem = kReads % kCopies;
+  // LDS read instructions of fragments [first, first + n)
+  auto read_insts = [](int first, int n) constexpr {
+    int c = 0;
+    for (int r = first; r < first + n; ++r) c += (r % (FM + FN) < FM || !kBT) ? kSub : 2;
+    return c;
+  };
   auto memory_phase = [&](int kt, int ct, int slot, bool live) {
     __builtin_amdgcn_sched_barrier(0);
     static_for<kCopies>([&](auto q) {
@@ -162,9 +223,10 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
       static_for<n>([&](auto u) { read_frag(kt, std::integral_constant<int, first + u>{}); });
     });
     static_for<kCopies>([&](auto q) {
+      constexpr int first = kPer * q + (q < kRem ? q : kRem);
       constexpr int n = kPer + (q < kRem ? 1 : 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, n * kSub, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, read_insts(first, n), 0);
     });
     advance_b(kt);
     __builtin_amdgcn_sched_barrier(0);
@@ -255,12 +317,23 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
 
 }  // namespace
 
-int launch_pingpong(const GemmParams& p0, int a_type, hipStream_t stream) {
+int launch_pingpong(const GemmParams& p0, int a_type, hipStream_t stream, bool bt) {
   GemmParams p = p0;
   int64_t grid;
   set_grid(p, 256, 256, &grid);
   if (grid <= 0) return TLA_OK;
   if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
+  if (bt) {
+    if (a_type == kBF16)
+      hipLaunchKernelGGL((gemm_pingpong_kernel<kBF16, true>), dim3((unsigned)grid), dim3(512), 0,
+                         stream, p);
+    else if (a_type == kF16)
+      hipLaunchKernelGGL((gemm_pingpong_kernel<kF16, true>), dim3((unsigned)grid), dim3(512), 0,
+                         stream, p);
+    else
+      return TLA_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
+  }
   switch (a_type) {
     case kBF16:
       hipLaunchKernelGGL(gemm_pingpong_kernel<kBF16>, dim3((unsigned)grid), dim3(512), 0, stream, p);
