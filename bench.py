@@ -520,13 +520,16 @@ def main():
         "transpose_frac_of_copy": round(tr_gbs / cp_gbs, 4)}
     del cdst
 
-    # The other two measured GEMMs, each timed on its own after the step loop
-    # (not part of a step): the fp8 8192^3 + GELU against the fp8 peak, and
-    # the launch-bound fp16 256^3.
+    # The other measured GEMMs, each timed on its own after the step loop
+    # (not part of a step): the fp8 8192^3 + GELU against the fp8 peak, the
+    # ragged fp16 3001 x 4097 x 777 with row-major B and odd pitches (the
+    # general kernel), and the launch-bound fp16 256^3.
     if not args.no_extra:
         cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds / 3
         out["fp8"] = extra_gemm(tla, W, W.GEMM_E4M3_8192, PEAK_FP8_TFLOPS, stream, args.warmup,
                                 K, cpu_s)
+        out["f16_ragged"] = extra_gemm(tla, W, W.GEMM_F16_RAGGED, PEAK_BF16_TFLOPS, stream,
+                                       args.warmup, K, cpu_s / 2)
         out["f16_256"] = extra_gemm(tla, W, W.GEMM_F16_256, PEAK_BF16_TFLOPS, stream,
                                     args.warmup, K, 0.0)
     if not args.no_cpu_baseline:

@@ -233,6 +233,31 @@ def test_misaligned_bases_take_general_path():
     _check_full(case, W.gemm_inputs(case), pad_front=1)
 
 
+@pytest.mark.parametrize("a_order,b_order", ORDERS)
+@pytest.mark.parametrize("a_type,pad", [(W.F16, 1), (W.BF16, 3), (W.E4M3, 1), (W.E4M3, 2),
+                                        (W.E4M3, 3)])
+def test_realigned_loads_bit_exact(a_order, b_order, a_type, pad):
+    """Bases shifted off alignment by `pad` elements (1 to 3 bytes for e4m3)
+    and odd pitches: the general kernel's whole-chunk loads from dword-aligned
+    pairs, funnel-shifted, for every byte offset of a row start; integer
+    inputs, so D is exact."""
+    M, N, K = 150, 140, 203
+    d_type = W.F16 if a_type == W.F16 else W.BF16
+    case = W.GemmCase(name="realign", M=M, N=N, K=K, a_type=a_type, b_type=a_type,
+                      d_type=d_type, a_order=a_order, b_order=b_order, alpha=1.5, beta=0.5,
+                      act=W.ACT_RELU, has_c=True, has_bias=True, seed=31 + pad,
+                      dist_a="int3", dist_b="int3", dist_c="int3", dist_bias="eighths")
+    case.lda += 1
+    case.ldb += 3
+    case.ldd += 1
+    assert G.variant(case) == "gemm_general_128x128"
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT[d_type], pad_front=pad)
+    assert G.padding_untouched(case, D, SENT[d_type])
+    want = W.encode(G.oracle_ref(case, inp), d_type).reshape(M, N)
+    assert np.array_equal(W.d_logical(case, D), want)
+
+
 def test_c_aliases_d():
     case = _small(M=200, N=136, K=64)
     inp = W.gemm_inputs(case)

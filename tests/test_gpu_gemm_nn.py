@@ -9,6 +9,8 @@ the oracle:
   with NaN padding;
 * the kernel choice: variant 1 at every size, variant 0 forcible (its own
   transpose-read form), variant 3 refused, the general kernel forcible;
+* the general kernel's own k-rows-of-n slab for pitches and bases off
+  16-byte alignment: N and K ragged down to one element, misaligned bases;
 * random inputs at 2048 x 2048 x 1024 and 4096 x 4096 x 512 within the
   tolerance.
 Tolerance: |D - ref| <= tol*(1 + |ref|), tol 1e-2.
@@ -69,6 +71,31 @@ def test_row_major_b_unaligned_pitch_takes_general_path():
     case.ldb += 3
     assert G.variant(case) == "gemm_general_128x128"
     _exact(case, W.gemm_inputs(case))
+
+
+GENERAL_SHAPES = [(1, 1, 1), (37, 7, 5), (64, 13, 64), (130, 129, 77), (300, 261, 200),
+                  (257, 1031, 131), (96, 4097, 40)]
+
+
+@pytest.mark.parametrize("a_type", [W.F16, W.BF16])
+@pytest.mark.parametrize("M,N,K", GENERAL_SHAPES)
+def test_general_kernel_row_major_b_bit_exact(M, N, K, a_type):
+    """Odd pitches for A, B, C and D and bases one element off alignment:
+    the general kernel with B's slab as k rows of n (chunks crossing N
+    element by element, rows past K zero)."""
+    case = _case(M, N, K, a_type, seed=M * 3 + N + K)
+    case.lda += 1
+    case.ldb += 1
+    case.ldc += 3
+    case.ldd += 1
+    assert G.variant(case) == "gemm_general_128x128"
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT, pad_front=1)
+    assert G.padding_untouched(case, D, SENT)
+    want = W.encode(G.oracle_ref(case, inp), case.d_type).reshape(case.M, case.N)
+    got = W.d_logical(case, D)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "%s: %d mismatches, first at %s" % ((M, N, K), len(bad), bad[0])
 
 
 @pytest.mark.parametrize("a_type", [W.F16, W.BF16])

@@ -17,8 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtla.so")
-SOURCES = ["api.cpp", "algebra.cpp", "gemm.hip", "gemm_pingpong.hip", "conv_slab.hip",
-           "transpose.hip", "layout_eval.hip"]
+SOURCES = ["api.cpp", "algebra.cpp", "gemm.hip", "gemm_general.hip", "gemm_pingpong.hip",
+           "conv_slab.hip", "transpose.hip", "layout_eval.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

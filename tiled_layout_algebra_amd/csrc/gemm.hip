@@ -1,6 +1,6 @@
-// gemm.hip -- the single-group GEMM kernels (128 x 128 and 256 x 256 block
-// tiles, direct-to-LDS or register-staged loads), the implicit-GEMM
-// convolution and the variant dispatch, for gfx950.
+// gemm.hip -- the single-group direct-to-LDS GEMM kernels (128 x 128 and
+// 256 x 256 block tiles), the implicit-GEMM convolution and the variant
+// dispatch, for gfx950.
 //
 //   D = act(alpha_eff * A.B + beta*C + bias),  fp32 accumulation.
 //
@@ -8,8 +8,9 @@
 // section 一: a workgroup owns a BM x BN tile of D (the block tile), each of
 // its 64-lane wavefronts a piece of it (the wave tile: 2 x 4 waves of
 // (BM/2) x (BN/4) in gemm_fast_kernel with 16-bit operands, 2 x 2 waves of
-// (BM/2) x (BN/2) in gemm_kernel, which serves e4m3, the register-staged
-// general path and the convolution), and each 32x32 MFMA instruction a
+// (BM/2) x (BN/2) in gemm_general.hip's kernel, which serves e4m3, the
+// register-staged general path and the convolution), and each 32x32 MFMA
+// instruction a
 // 32x32 piece of that (the instruction tile).  The K loop (section 二's
 // mainloop: global -> shared -> register) moves one 128-byte-wide K slab of
 // A and of B per step into LDS (64 bf16/fp16 or 128 e4m3 per row), with two
@@ -20,16 +21,17 @@
 // before the store).  The two-group 256 x 256 kernel the dispatch prefers
 // for large problems lives in gemm_pingpong.hip.
 //
-// Two load paths feed the same LDS layout:
+// Load paths:
 //   fast    both operands K-contiguous, 16-byte aligned rows, K a multiple of
 //           the slab width: each lane issues a direct HBM -> LDS copy that
 //           lands lane-linearly; the LDS XOR swizzle is applied by permuting
 //           which global chunk each lane fetches.  Rows past M or N are
 //           clamped to the last real row (their results are never stored),
 //           so the loop carries no predicates.
-//   general any order, pitch or alignment, ragged K: registers staged through
-//           a strip-mined thread map with per-element predicates; elements
-//           outside the matrix load as zero.
+//   general any order, pitch or alignment, ragged K (gemm_general.hip):
+//           registers staged through a strip-mined thread map with
+//           per-element predicates; elements outside the matrix load as
+//           zero.
 #include "gemm_common.hpp"
 
 namespace tla {
@@ -309,167 +311,6 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
                          kLdsEpi ? smem + wave * WM * 64 * FN : nullptr);
 }
 
-// ------------------------------------------------------------------ kernel
-// kStages LDS stages of BM + BN rows of kRowBytes bytes each.  K-tile kt
-// lives in stage kt % kStages; up to kStages - 1 tiles are in flight, so the
-// copy of a tile has kStages - 1 tiles of matrix-core work to arrive in.
-template <int kCode, int BM, int BN, int kRowBytes, int kStages, bool kFast, bool kConv = false>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
-  using Atom = MfmaAtom<kCode>;
-  using Frag = typename Atom::Frag;
-  constexpr int EB = elem_bytes(kCode);
-  constexpr int BK = kRowBytes / EB;         // K elements per k-tile
-  constexpr int WM = BM / 2, WN = BN / 2;    // 2 x 2 wavefronts
-  constexpr int FM = WM / 32, FN = WN / 32;  // MFMA tiles per wave
-  constexpr int KSTEPS = BK / Atom::kK;
-  static_assert(KSTEPS >= 1 && BK % Atom::kK == 0, "slab narrower than one MFMA step");
-  constexpr int SLAB_A = BM * kRowBytes, STAGE = (BM + BN) * kRowBytes;
-  static_assert(kStages * STAGE <= 160 * 1024, "LDS budget");
-  // global_load_lds instructions one thread issues per k-tile
-  constexpr int kLoadsPerTile = (BM + BN) * kRowBytes / 16 / kThreads;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * STAGE];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int tm, tn;
-  schedule(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int wm0 = (wave & 1) * WM, wn0 = (wave >> 1) * WN;
-
-  f32x16 acc[FM][FN];
-  static_for<FM>([&](auto i) { static_for<FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
-
-  // Fragment double buffer and the pieces of one MFMA k-step.
-  Frag a[2][FM], b[2][FN];
-  auto read_frags = [&](auto buf, const uint8_t* stage, auto ks) {
-    static_for<FM>([&](auto i) {
-      a[buf][i] = load_frag<kCode, kRowBytes>(stage, wm0 + 32 * i + (lane & 31), ks, lane);
-    });
-    static_for<FN>([&](auto j) {
-      b[buf][j] = load_frag<kCode, kRowBytes>(stage + SLAB_A, wn0 + 32 * j + (lane & 31), ks, lane);
-    });
-  };
-  // MFMAs number lo .. hi-1 of a step (i major, j minor)
-  auto mfmas = [&](auto buf, auto lo, auto hi) {
-    static_for<hi - lo>([&](auto q) {
-      constexpr int idx = lo + q;
-      Atom::mma(acc[idx / FN][idx % FN], b[buf][idx % FN], a[buf][idx / FN]);
-    });
-  };
-  constexpr int kReads = (FM + FN) * (Atom::kLaneBytes / 16);
-  constexpr int kMfmas = FM * FN;
-
-  const int KT = (p.K + BK - 1) / BK;
-  if constexpr (kFast) {
-    // One software pipeline over all k-steps.  The fragments of step g+1 are
-    // read at the start of step g, a whole step of MFMAs before use.  In the
-    // last step of k-tile kt, half-way through its MFMAs, every wave waits
-    // for tile kt+1 and meets at a barrier; that barrier also proves every
-    // wave is done reading tile kt's stage, which is refilled at once with
-    // tile kt+kStages.
-    static_assert(KSTEPS % 2 == 0, "fragment buffers alternate per step");
-    const int64_t a_rb = p.a_sr * EB, b_rb = p.b_sr * EB;
-    auto issue = [&](int kt) {
-      uint8_t* st = smem + (kt % kStages) * STAGE;
-      const int64_t kb = (int64_t)kt * kRowBytes;
-      dma_slab<BM, kRowBytes>(p.A, a_rb, m0, p.M, kb, st, tid);
-      dma_slab<BN, kRowBytes>(p.B, b_rb, n0, p.N, kb, st + SLAB_A, tid);
-    };
-    // wait until tile `t` has landed, given tiles up to `last_issued` were issued
-    auto wait_tile = [&](int t, int last_issued) {
-      const int after = min(kStages - 1, last_issued - t);
-      static_for<kStages>([&](auto n) {
-        if (after == n) wait_vmcnt<n * kLoadsPerTile>();
-      });
-    };
-    static_for<kStages>([&](auto s) {
-      if (s < KT) issue(s);
-    });
-    if (KT > 0) {
-      wait_tile(0, min(kStages, KT) - 1);
-      __syncthreads();
-      read_frags(std::integral_constant<int, 0>{}, smem, std::integral_constant<int, 0>{});
-    }
-    for (int kt = 0; kt < KT; ++kt) {
-      const uint8_t* stage = smem + (kt % kStages) * STAGE;
-      static_for<KSTEPS>([&](auto ks) {
-        constexpr int cur = ks & 1;
-        if constexpr (ks + 1 < KSTEPS) {
-          read_frags(std::integral_constant<int, cur ^ 1>{}, stage,
-                     std::integral_constant<int, ks + 1>{});
-          mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
-                std::integral_constant<int, kMfmas>{});
-          __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, kMfmas, 0);
-        } else {
-          mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
-                std::integral_constant<int, kMfmas / 2>{});
-          if (kt + 1 < KT) {
-            // tiles issued so far: 0 .. min(kt + kStages - 1, KT - 1)
-            wait_tile(kt + 1, min(kt + kStages - 1, KT - 1));
-            __syncthreads();
-            if (kt + kStages < KT) issue(kt + kStages);
-            read_frags(std::integral_constant<int, cur ^ 1>{},
-                       smem + ((kt + 1) % kStages) * STAGE, std::integral_constant<int, 0>{});
-          }
-          mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, kMfmas / 2>{},
-                std::integral_constant<int, kMfmas>{});
-        }
-      });
-    }
-  } else {
-    static_assert(kStages == 2, "register-staged path double-buffers");
-    // k-steps of one tile from LDS, fragments of step ks+1 read during ks
-    auto compute = [&](const uint8_t* stage) {
-      read_frags(std::integral_constant<int, 0>{}, stage, std::integral_constant<int, 0>{});
-      static_for<KSTEPS>([&](auto ks) {
-        constexpr int cur = ks & 1;
-        if constexpr (ks + 1 < KSTEPS)
-          read_frags(std::integral_constant<int, cur ^ 1>{}, stage,
-                     std::integral_constant<int, ks + 1>{});
-        mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
-              std::integral_constant<int, kMfmas>{});
-      });
-    };
-    static_assert(!kConv || !kFast, "the convolution view uses the register-staged path");
-    std::conditional_t<kConv, ConvSlab<BM, EB, kRowBytes>, RegSlab<BM, EB, kRowBytes>> ra;
-    RegSlab<BN, EB, kRowBytes> rb;
-    const bool a_vec = (p.flags >> 8) & 1, b_vec = (p.flags >> 9) & 1;
-    const bool a_kc = (p.a_sk == 1), b_kc = (p.b_sk == 1);
-    if (KT > 0) {
-      if constexpr (kConv) ra.load_conv(p, m0, 0, a_vec, tid);
-      else ra.load(p.A, p.a_sr, p.a_sk, m0, p.M, 0, p.K, a_vec, tid);
-      rb.load(p.B, p.b_sr, p.b_sk, n0, p.N, 0, p.K, b_vec, tid);
-      ra.store(smem, kConv || a_kc, tid);
-      rb.store(smem + SLAB_A, b_kc, tid);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      uint8_t* cur = smem + (kt & 1) * STAGE;
-      uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
-      if (kt + 1 < KT) {
-        if constexpr (kConv) ra.load_conv(p, m0, (kt + 1) * BK, a_vec, tid);
-        else ra.load(p.A, p.a_sr, p.a_sk, m0, p.M, (kt + 1) * BK, p.K, a_vec, tid);
-        rb.load(p.B, p.b_sr, p.b_sk, n0, p.N, (kt + 1) * BK, p.K, b_vec, tid);
-      }
-      compute(cur);
-      if (kt + 1 < KT) {
-        ra.store(nxt, kConv || a_kc, tid);
-        rb.store(nxt + SLAB_A, b_kc, tid);
-      }
-      __syncthreads();
-    }
-  }
-
-  // Epilogue: acc[i][j] holds the D^T piece for rows m0+wm0+32i.. and
-  // columns n0+wn0+32j..; value r of lane l sits at (row, col) =
-  // (lane%32, mfma32_acc_row(l, r)) of that 32x32 piece.  No copy is in
-  // flight here; after the barrier the stages are the waves' regions.
-  constexpr bool kLdsEpi = 4 * WM * 64 * FN <= kStages * STAGE;
-  __syncthreads();
-  epilogue_tiles<FM, FN>(p, m0 + wm0, n0 + wn0, lane, acc,
-                         kLdsEpi ? smem + wave * WM * 64 * FN : nullptr);
-}
-
 // ----------------------------------------------------------------- dispatch
 template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront, int kWM, int kWN,
           bool kConv = false, bool kBT = false>
@@ -482,18 +323,6 @@ int launch_fast(const GemmParams& p0, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_fast_kernel<kCode, BM, BN, kRowBytes, kStages, kFront, kWM, kWN, kConv,
                                        kBT>),
                      dim3((unsigned)grid), dim3(64 * kWM * kWN), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
-}
-
-template <int kCode, int BM, int BN, int kRowBytes, bool kFast>
-int launch_two_stage(const GemmParams& p0, hipStream_t stream) {
-  GemmParams p = p0;
-  int64_t grid;
-  set_grid(p, BM, BN, &grid);
-  if (grid <= 0) return TLA_OK;
-  if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((gemm_kernel<kCode, BM, BN, kRowBytes, 2, kFast>), dim3((unsigned)grid),
-                     dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
 }
 
@@ -537,15 +366,15 @@ int dispatch_typed(const GemmParams& p, bool fast, bool bt, bool big, hipStream_
   }
   if (v == 0) return launch_pingpong(p, kCode, s);
   if constexpr (kCode == kE4M3) {
-    if (v == 3) return launch_two_stage<kCode, 256, 256, 128, true>(p, s);
-    if (v == 1) return launch_two_stage<kCode, 128, 128, 128, true>(p, s);
+    if (v == 3) return launch_two_stage_e4m3(p, true, s);
+    if (v == 1) return launch_two_stage_e4m3(p, false, s);
   } else {
     if (v == 3) return launch_fast<kCode, 256, 256, 128, 2, 1, 2, 4>(p, s);
     // 8 wavefronts of 64 x 32 (two per SIMD): 9.2 us at 1024^3 and 20.3 us
     // at 2048^3, against 11.1 and 21.7 us for 4 wavefronts of 64 x 64
     if (v == 1) return launch_fast<kCode, 128, 128, 128, 3, 1, 2, 4>(p, s);
   }
-  return launch_two_stage<kCode, 128, 128, 128, false>(p, s);
+  return launch_general(p, kCode, s);
 }
 
 // The kernel each variant launches for operand type kCode.
@@ -557,8 +386,8 @@ const void* variant_kernel(int v, int* threads) {
     return pingpong_kernel(kCode);
   }
   if constexpr (kCode == kE4M3) {
-    if (v == 3) return (const void*)gemm_kernel<kCode, 256, 256, 128, 2, true>;
-    if (v == 1) return (const void*)gemm_kernel<kCode, 128, 128, 128, 2, true>;
+    if (v == 3) return two_stage_e4m3_kernel(true);
+    if (v == 1) return two_stage_e4m3_kernel(false);
   } else {
     if (v == 3) {
       *threads = 512;
@@ -569,7 +398,7 @@ const void* variant_kernel(int v, int* threads) {
       return (const void*)gemm_fast_kernel<kCode, 128, 128, 128, 3, 1, 2, 4>;
     }
   }
-  return (const void*)gemm_kernel<kCode, 128, 128, 128, 2, false>;
+  return general_kernel(kCode);
 }
 
 }  // namespace
@@ -649,17 +478,7 @@ int conv_dispatch(const ConvProblem& c, hipStream_t stream, int forced) {
     return narrow ? launch_fast<kF16, 256, 64, 128, 2, 1, 4, 2, true>(p, stream)
                   : launch_fast<kF16, 128, 128, 128, 2, 1, 2, 2, true>(p, stream);
   }
-  int64_t grid;
-  set_grid(p, 128, 128, &grid);
-  if (grid <= 0) return TLA_OK;
-  if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
-  if (c.type == TLA_BF16)
-    hipLaunchKernelGGL((gemm_kernel<kBF16, 128, 128, 128, 2, false, true>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm_kernel<kF16, 128, 128, 128, 2, false, true>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
+  return launch_conv_general(p, c.type, stream);
 }
 
 int gemm_variant_info(int a_type, int variant, GemmKernelInfo* out) {
@@ -720,10 +539,16 @@ int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const 
   if (g.d_order == TLA_ROW_MAJOR && (g.ldd % 4) == 0 && aligned(g.D, 8)) p.flags |= kDVec;
   if (g.C && ceb == 2 && g.c_order == TLA_ROW_MAJOR && (g.ldc % 8) == 0 && aligned(g.C, 16)) p.flags |= kC16;
   if (g.d_order == TLA_ROW_MAJOR && (g.ldd % 8) == 0 && aligned(g.D, 16)) p.flags |= kD16;
+  if (g.C && ceb == 2 && g.c_order == TLA_ROW_MAJOR && aligned(g.C, 2)) p.flags |= kC2;
+  if (g.d_order == TLA_ROW_MAJOR && aligned(g.D, 2)) p.flags |= kD2;
   if (g.bias && aligned(g.bias, 4 * beb)) p.flags |= kBiasVec;
   const bool a_vec = (g.a_order == TLA_ROW_MAJOR) && ((g.lda * eb) % 16 == 0) && aligned(g.A, 16);
-  const bool b_vec = (g.b_order == TLA_COL_MAJOR) && ((g.ldb * eb) % 16 == 0) && aligned(g.B, 16);
-  p.flags |= (a_vec ? 1 << 8 : 0) | (b_vec ? 1 << 9 : 0);
+  const bool b_rows16 = ((g.ldb * eb) % 16 == 0) && aligned(g.B, 16);
+  const bool b_vec = (g.b_order == TLA_COL_MAJOR) && b_rows16;
+  // 16-bit N-contiguous B (the general kernel reads it by rows of n)
+  const bool nt = eb == 2 && g.b_order == TLA_ROW_MAJOR;
+  // bit 9: B's contiguous runs (K runs, or N runs when nt) are 16-byte aligned
+  p.flags |= (a_vec ? 1 << 8 : 0) | ((b_vec || (nt && b_rows16)) ? 1 << 9 : 0);
   const int BK = fast_slab_bytes(g.a_type) / eb;
   // the fast kernel addresses each operand with 32-bit offsets below 2^31
   const bool small_ops = (int64_t)g.M * g.lda * eb < (int64_t(1) << 31) &&
@@ -731,8 +556,7 @@ int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const 
   const bool fast = a_vec && b_vec && small_ops && g.K > 0 && (g.K % BK) == 0;
   // A in the fast layout, B a 16-bit row-major K x N matrix with 16-byte
   // aligned rows and whole 16-byte chunks of columns, below 2 GiB
-  const bool bt = !fast && eb == 2 && a_vec && g.b_order == TLA_ROW_MAJOR &&
-                  ((g.ldb * eb) % 16) == 0 && aligned(g.B, 16) && g.N % 8 == 0 &&
+  const bool bt = !fast && nt && a_vec && b_rows16 && g.N % 8 == 0 &&
                   (int64_t)g.M * g.lda * eb < (int64_t(1) << 31) &&
                   (int64_t)g.K * g.ldb * eb < (int64_t(1) << 31) && g.K > 0 && (g.K % BK) == 0;
   const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256);

@@ -21,8 +21,9 @@
 namespace tla {
 
 // p.flags: C / D / bias rows allow aligned 4-element (8-byte for 16-bit)
-// vectors; C / D rows (16-bit) allow aligned 16-byte vectors.
-enum : int { kCVec = 1, kDVec = 2, kBiasVec = 4, kC16 = 8, kD16 = 16 };
+// vectors; C / D rows (16-bit) allow aligned 16-byte vectors; C / D are
+// row-major 16-bit matrices at an even address (any pitch).
+enum : int { kCVec = 1, kDVec = 2, kBiasVec = 4, kC16 = 8, kD16 = 16, kC2 = 32, kD2 = 64 };
 
 struct GemmParams {
   const uint8_t* A;
@@ -51,6 +52,20 @@ struct GemmParams {
 // rows, N a multiple of 8).
 int launch_pingpong(const GemmParams& p, int a_type, hipStream_t stream, bool bt = false);
 const void* pingpong_kernel(int a_type);
+
+// The four-wavefront kernel of gemm_general.hip.  launch_general: its
+// register-staged form, 128 x 128 tiles, any order, pitch, alignment and
+// ragged K (the operand views are read from p's strides).
+// launch_two_stage_e4m3: its direct-to-LDS form for e4m3 in the fast layout,
+// 256 x 256 (big) or 128 x 128 tiles.  launch_conv_general: the register-
+// staged implicit-GEMM convolution (16-bit; p holds the convolution view).
+// general_kernel / two_stage_e4m3_kernel: the kernels those launch for
+// K-contiguous operands, for occupancy queries.
+int launch_general(const GemmParams& p, int type, hipStream_t stream);
+int launch_two_stage_e4m3(const GemmParams& p, bool big, hipStream_t stream);
+int launch_conv_general(const GemmParams& p, int type, hipStream_t stream);
+const void* general_kernel(int type);
+const void* two_stage_e4m3_kernel(bool big);
 
 namespace {
 
@@ -166,36 +181,77 @@ __device__ __forceinline__ void dma_one(const uint8_t* __restrict__ base, int64_
 }
 
 // --------------------------------------------------------- general loader
-// Element-predicated, register-staged slab copy for any operand view
-// (row, k) -> row*s_r + k*s_k.  K-contiguous views use the row-contiguous
-// thread map (consecutive lanes walk K); the others use the column-major
-// variant (consecutive lanes walk rows, so each element load coalesces).
-template <int ROWS, int EB, int kRowBytes>
+// 16 bytes from any byte address p through dword-aligned loads: the 16
+// aligned bytes at or below p (lo) and the dword holding p + 15 (hi); the
+// return value is p % 4.  Each dword read holds at least one of the 16
+// requested bytes, so the reads never leave the pages those bytes live on.
+// When p is dword-aligned, hi re-reads the last dword of lo.  The loads are
+// only issued here: realign16 shifts the bytes into place once they are
+// needed, so a register-staged copy does not wait for them early.
+__device__ __forceinline__ uint32_t load16_split(const uint8_t* p, i32x4& lo, uint32_t& hi) {
+  typedef int i32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+  const uint32_t sh = (uint32_t)(uintptr_t)p & 3u;
+  const uint8_t* q = p - sh;
+  lo = *(const i32x4_a4*)q;
+  hi = *(const uint32_t*)(q + (sh ? 16 : 12));
+  return sh;
+}
+
+// The 16 bytes load16_split fetched, funnel-shifted down by sh bytes
+// (v_alignbyte_b32 takes the high dword first and reads only sh's low two
+// bits); sh = 0 returns lo.
+__device__ __forceinline__ i32x4 realign16(const i32x4& lo, uint32_t hi, uint32_t sh) {
+  const uint32_t w0 = lo[0], w1 = lo[1], w2 = lo[2], w3 = lo[3];
+  i32x4 r;
+  r[0] = (int)__builtin_amdgcn_alignbyte(w1, w0, sh);
+  r[1] = (int)__builtin_amdgcn_alignbyte(w2, w1, sh);
+  r[2] = (int)__builtin_amdgcn_alignbyte(w3, w2, sh);
+  r[3] = (int)__builtin_amdgcn_alignbyte(hi, w3, sh);
+  return r;
+}
+
+// Element-predicated, register-staged slab copy of an operand view
+// (row, k) -> row*s_r + k*s_k, fixed at compile time to one of the two
+// views the library builds: kKC (K-contiguous, s_k = 1) or row-contiguous
+// (s_r = 1, an M- or N-contiguous matrix).  K-contiguous views use the
+// row-contiguous thread map (consecutive lanes walk K) and move whole
+// 16-byte chunks -- one 16-byte load when the rows are 16-byte aligned, the
+// dword-aligned pair of load16_split otherwise (shifted into place by
+// store) -- and only the chunk that crosses K element by element; the
+// others use the column-major variant (consecutive lanes walk rows, so each
+// element load coalesces) and move every chunk element by element.  Rows
+// past rows_valid and elements past K load as zero.
+template <int ROWS, int EB, int kRowBytes, bool kKC>
 struct RegSlab {
   using Swz = typename Slab<kRowBytes>::Swz;
   static constexpr int kChunks = Slab<kRowBytes>::kChunks;
   static constexpr int kI = ROWS * kChunks / kThreads;
   static constexpr int kCE = 16 / EB;  // elements per 16-byte chunk
+  static_assert(kI <= 8, "byte shifts pack 4 bits per chunk");
   i32x4 v[kI];
+  uint32_t hi[kI];
+  uint32_t shifts;  // byte shift of chunk it in bits 4 it .. 4 it + 1
 
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t s_r, int64_t s_k,
-                                       int row0, int rows_valid, int k0, int K, bool vec_ok,
-                                       int tid) {
-    constexpr StripMinedMap kmap(ROWS, kChunks, kThreads, 1, kI, 1);
-    constexpr StripMinedMap rmap(ROWS, kChunks, kThreads, 1, kI, 0);
-    static_assert(kmap.well_formed() && rmap.well_formed(), "slab thread maps");
-    const bool kcontig = (s_k == 1);
+  // s: the row stride (kKC) or the k stride (otherwise), in elements
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t s, int row0,
+                                       int rows_valid, int k0, int K, bool vec_ok, int tid) {
+    constexpr StripMinedMap map(ROWS, kChunks, kThreads, 1, kI, kKC ? 1 : 0);
+    static_assert(map.well_formed(), "slab thread map");
+    shifts = 0;
 #pragma unroll
     for (int it = 0; it < kI; ++it) {
-      const int r = kcontig ? kmap.row(tid, it, 0) : rmap.row(tid, it, 0);
-      const int c = kcontig ? kmap.col(tid, it, 0) : rmap.col(tid, it, 0);
-      const int gr = row0 + r;
-      const int gk = k0 + c * kCE;
+      const int gr = row0 + map.row(tid, it, 0);
+      const int gk = k0 + map.col(tid, it, 0) * kCE;
       i32x4 x = {0, 0, 0, 0};
+      uint32_t h = 0;
       if (gr < rows_valid) {
+        const int64_t s_r = kKC ? s : 1, s_k = kKC ? 1 : s;
         const uint8_t* p = base + (gr * s_r + (int64_t)gk * s_k) * EB;
-        if (vec_ok && kcontig && gk + kCE <= K) {
-          x = *(const i32x4*)p;
+        if (kKC && gk + kCE <= K) {
+          if (vec_ok)
+            x = *(const i32x4*)p;
+          else
+            shifts |= load16_split(p, x, h) << (4 * it);
         } else {
           uint8_t bytes[16] = {};
 #pragma unroll
@@ -210,20 +266,108 @@ struct RegSlab {
         }
       }
       v[it] = x;
+      hi[it] = h;
     }
   }
 
-  __device__ __forceinline__ void store(uint8_t* slab, bool kcontig, int tid) const {
-    constexpr StripMinedMap kmap(ROWS, kChunks, kThreads, 1, kI, 1);
-    constexpr StripMinedMap rmap(ROWS, kChunks, kThreads, 1, kI, 0);
+  // realign: some chunks came through load16_split (rows not 16-byte aligned)
+  __device__ __forceinline__ void store(uint8_t* slab, bool realign, int tid) const {
+    constexpr StripMinedMap map(ROWS, kChunks, kThreads, 1, kI, kKC ? 1 : 0);
 #pragma unroll
     for (int it = 0; it < kI; ++it) {
-      const int r = kcontig ? kmap.row(tid, it, 0) : rmap.row(tid, it, 0);
-      const int c = kcontig ? kmap.col(tid, it, 0) : rmap.col(tid, it, 0);
-      *(i32x4*)(slab + r * kRowBytes + Swz::chunk(r, c) * 16) = v[it];
+      const int r = map.row(tid, it, 0), c = map.col(tid, it, 0);
+      *(i32x4*)(slab + r * kRowBytes + Swz::chunk(r, c) * 16) =
+          (kKC && realign) ? realign16(v[it], hi[it], shifts >> (4 * it)) : v[it];
     }
   }
 };
+
+// N-contiguous 16-bit B (a row-major K x N matrix, pitch ld elements) for
+// the register-staged kernel.  The slab is BK rows of k, each BN columns of
+// n (2 BN bytes; 16-byte chunk c of row r stored at chunk c ^ 4 (r % 4)),
+// and load_frag_nt reads it back with ds_read_b64_tr_b16.  Consecutive
+// lanes walk the chunks of one k row, so a load instruction covers runs of
+// whole rows; full chunks move as 16 bytes (one load on 16-byte aligned
+// rows, load16_split otherwise), the chunk that crosses N element by element,
+// and rows past K and columns past N load as zero.
+template <int BN, int BK>
+struct RegSlabNT {
+  static constexpr int kRow = 2 * BN;
+  static constexpr int kCh = kRow / 16;
+  static constexpr int kI = BK * kCh / kThreads;
+  static_assert(kI * kThreads == BK * kCh, "whole chunks per thread");
+  static_assert(kCh >= 16 && kCh % 16 == 0, "the swizzle permutes chunks within 16");
+  static_assert(kI <= 8, "byte shifts pack 4 bits per chunk");
+  i32x4 v[kI];
+  uint32_t hi[kI];
+  uint32_t shifts;  // byte shift of chunk it in bits 4 it .. 4 it + 1
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t ld, int n0, int N,
+                                       int k0, int K, bool vec_ok, int tid) {
+    shifts = 0;
+#pragma unroll
+    for (int it = 0; it < kI; ++it) {
+      const int sc = tid + kThreads * it, r = sc / kCh, c = sc % kCh;
+      const int gk = k0 + r, gn = n0 + 8 * c;
+      i32x4 x = {0, 0, 0, 0};
+      uint32_t h = 0;
+      if (gk < K && gn < N) {
+        const uint8_t* p = base + ((int64_t)gk * ld + gn) * 2;
+        if (gn + 8 <= N) {
+          if (vec_ok)
+            x = *(const i32x4*)p;
+          else
+            shifts |= load16_split(p, x, h) << (4 * it);
+        } else {
+          uint8_t bytes[16] = {};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (gn + e < N) {
+              bytes[2 * e] = p[2 * e];
+              bytes[2 * e + 1] = p[2 * e + 1];
+            }
+          }
+          x = __builtin_bit_cast(i32x4, bytes);
+        }
+      }
+      v[it] = x;
+      hi[it] = h;
+    }
+  }
+
+  // realign: some chunks came through load16_split (rows not 16-byte aligned)
+  __device__ __forceinline__ void store(uint8_t* slab, bool realign, int tid) const {
+#pragma unroll
+    for (int it = 0; it < kI; ++it) {
+      const int sc = tid + kThreads * it, r = sc / kCh, c = sc % kCh;
+      *(i32x4*)(slab + r * kRow + (c ^ (4 * (r & 3))) * 16) =
+          realign ? realign16(v[it], hi[it], shifts >> (4 * it)) : v[it];
+    }
+  }
+};
+
+// The B fragment of 32x32x16 MFMA k-step ks for columns col0 .. col0 + 31
+// of a RegSlabNT slab (rows of kRow bytes): lane l gets column col0 + l % 32,
+// k = 16 ks + 8 (l / 32) .. + 7, as two ds_read_b64_tr_b16.  In a
+// quarter-wave the instruction hands lane j element e of the 8 bytes that
+// lane 4 e + j / 4 addresses, at position j % 4, so lane a of the quarter
+// addresses row k0 + a / 4, columns n0 + 4 (a % 4) .. + 3, and lane j
+// receives B[k0 .. k0 + 3][n0 + j].  Rows k0 .. k0 + 3 of one 32-column
+// half-wave land on 16 distinct 16-byte bank groups under the swizzle.
+template <int kRow>
+__device__ __forceinline__ i32x4 load_frag_nt(const uint8_t* slab, int col0, int ks, int lane) {
+  typedef int s32x2 __attribute__((ext_vector_type(2)));
+  const int qw = lane >> 4, a4 = lane & 15;
+  const int n = col0 + 16 * (qw & 1) + 4 * (a4 & 3);
+  s32x2 h[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int k = 16 * ks + 8 * (qw >> 1) + 4 * hh + (a4 >> 2);
+    h[hh] = __builtin_bit_cast(
+        s32x2, ds_read_tr16(slab + k * kRow + ((n >> 3) ^ (4 * (k & 3))) * 16 + (n & 7) * 2));
+  }
+  return i32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+}
 
 // ---------------------------------------------- implicit-GEMM A loader
 // The A operand of a convolution seen as a GEMM (the implicit GEMM of the
@@ -236,8 +380,8 @@ struct RegSlab {
 // (and the image is 16-byte aligned) a 16-byte chunk never straddles a
 // filter position, so one bounds check covers it.
 template <int ROWS, int EB, int kRowBytes>
-struct ConvSlab : RegSlab<ROWS, EB, kRowBytes> {
-  using Base = RegSlab<ROWS, EB, kRowBytes>;
+struct ConvSlab : RegSlab<ROWS, EB, kRowBytes, true> {
+  using Base = RegSlab<ROWS, EB, kRowBytes, true>;
 
   __device__ __forceinline__ const uint8_t* at(const GemmParams& p, int n, int h0, int w0,
                                                int k) const {
@@ -524,6 +668,77 @@ __device__ __forceinline__ void epilogue_lds(const GemmParams& p, int m_base, in
   });
 }
 
+// 16 bytes to an even address p: one 16-byte store when p is dword-aligned,
+// else a 2-byte, a 12-byte (dword-aligned) and a 2-byte store, so no byte
+// outside [p, p + 16) is written.
+__device__ __forceinline__ void store16_even(uint8_t* p, const i32x4& v) {
+  typedef int i32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+  typedef int i32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
+  if (((uint32_t)(uintptr_t)p & 2u) == 0) {
+    *(i32x4_a4*)p = v;
+  } else {
+    const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+    i32x3_a4 mid;
+    mid[0] = (int)__builtin_amdgcn_alignbyte(w1, w0, 2);
+    mid[1] = (int)__builtin_amdgcn_alignbyte(w2, w1, 2);
+    mid[2] = (int)__builtin_amdgcn_alignbyte(w3, w2, 2);
+    *(uint16_t*)p = (uint16_t)w0;
+    *(i32x3_a4*)(p + 2) = mid;
+    *(uint16_t*)(p + 14) = (uint16_t)(w3 >> 16);
+  }
+}
+
+// epilogue_lds for C and D rows at any even address (any pitch): the wave
+// reads its C sub-tile row by row with realigned 16-byte loads
+// (load16_split) and writes it into its region in the same swizzled layout,
+// and stores D row by row through store16_even.  Consecutive lanes cover a
+// row's consecutive chunks, so each access instruction spans whole rows
+// instead of 32 rows 8 bytes apart.
+template <int kAct, bool kDBf16, bool kHasC, int FM, int FN>
+__device__ __forceinline__ void epilogue_lds_any(const GemmParams& p, int m_base, int n_base,
+                                                 int lane, const f32x16 (&acc)[FM][FN],
+                                                 uint8_t* region) {
+  constexpr int kRowB = 64 * FN, kCh = kRowB / 16, kRowsPerKiB = 1024 / kRowB;
+  static_assert(kCh == 4 || kCh == 8 || kCh == 16, "row width");
+  constexpr int kIters = 32 * FM * kRowB / 1024;
+  static_assert(kIters <= 8, "byte shifts pack 4 bits per row chunk");
+  auto swz = [](int r, int c) { return c ^ ((r / (16 / kCh)) & (kCh - 1)); };
+  const int row = lane & 31, half = lane >> 5;
+  const int rr = lane / kCh, cs = lane % kCh;  // row-wise view of one KiB
+  if constexpr (kHasC) {
+    const uint8_t* C = p.C + ((int64_t)m_base * p.c_sm + n_base) * 2;
+    i32x4 lo[kIters];
+    uint32_t hi[kIters], shifts = 0;
+    static_for<kIters>([&](auto t) {
+      const int r = kRowsPerKiB * t + rr;
+      shifts |= load16_split(C + (int64_t)r * p.c_sm * 2 + swz(r, cs) * 16, lo[t], hi[t]) << (4 * t);
+    });
+    static_for<kIters>([&](auto t) {
+      *(i32x4*)(region + t * 1024 + lane * 16) = realign16(lo[t], hi[t], shifts >> (4 * t));
+    });
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
+  uint2 braw[FN][4];
+  load_bias16<FN>(p, n_base, half, braw);
+  static_for<FM>([&](auto i) {
+    static_for<FN>([&](auto j) {
+      static_for<4>([&](auto g) {
+        const int r = 32 * i + row;
+        uint8_t* slot = region + r * kRowB + swz(r, 4 * j + g) * 16 + 8 * half;
+        const uint2 c = kHasC ? *(const uint2*)slot : uint2{0u, 0u};
+        *(uint2*)slot = epi_group<kAct, kDBf16, kHasC>(acc[i][j], g, c, braw[j][g], p.alpha, p.beta);
+      });
+    });
+  });
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  uint8_t* D = p.D + ((int64_t)m_base * p.d_sm + n_base) * 2;
+  static_for<kIters>([&](auto t) {
+    const int r = kRowsPerKiB * t + rr;
+    const i32x4 v = *(const i32x4*)(region + t * 1024 + lane * 16);
+    store16_even(D + (int64_t)r * p.d_sm * 2 + swz(r, cs) * 16, v);
+  });
+}
+
 // Full wave tile straight from and to global memory with 8-byte vectors;
 // all C and bias loads are issued before the arithmetic.
 template <int kAct, bool kDBf16, bool kHasC, int FM, int FN>
@@ -559,35 +774,40 @@ __device__ __forceinline__ void epilogue_direct(const GemmParams& p, int m_base,
   });
 }
 
-template <bool kLds, int kAct, bool kDBf16, int FM, int FN>
+// kForm: 0 direct, 1 LDS with 16-byte aligned rows, 2 LDS with rows at any
+// even address
+template <int kForm, int kAct, bool kDBf16, int FM, int FN>
 __device__ __forceinline__ void epilogue_fast(const GemmParams& p, int m_base, int n_base, int lane,
                                               const f32x16 (&acc)[FM][FN], uint8_t* region) {
   const bool has_c = p.beta != 0.f;
-  if constexpr (kLds) {
+  if constexpr (kForm == 1) {
     if (has_c) epilogue_lds<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc, region);
     else epilogue_lds<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc, region);
+  } else if constexpr (kForm == 2) {
+    if (has_c) epilogue_lds_any<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc, region);
+    else epilogue_lds_any<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc, region);
   } else {
     if (has_c) epilogue_direct<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc);
     else epilogue_direct<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc);
   }
 }
 
-template <bool kLds, int FM, int FN>
+template <int kForm, int FM, int FN>
 __device__ __forceinline__ void epilogue_switch(const GemmParams& p, int m_base, int n_base, int lane,
                                                 const f32x16 (&acc)[FM][FN], uint8_t* region) {
   const bool dbf = p.d_type == kBF16;
   switch (p.act) {
     case TLA_ACT_RELU:
-      if (dbf) epilogue_fast<kLds, TLA_ACT_RELU, true>(p, m_base, n_base, lane, acc, region);
-      else epilogue_fast<kLds, TLA_ACT_RELU, false>(p, m_base, n_base, lane, acc, region);
+      if (dbf) epilogue_fast<kForm, TLA_ACT_RELU, true>(p, m_base, n_base, lane, acc, region);
+      else epilogue_fast<kForm, TLA_ACT_RELU, false>(p, m_base, n_base, lane, acc, region);
       break;
     case TLA_ACT_GELU:
-      if (dbf) epilogue_fast<kLds, TLA_ACT_GELU, true>(p, m_base, n_base, lane, acc, region);
-      else epilogue_fast<kLds, TLA_ACT_GELU, false>(p, m_base, n_base, lane, acc, region);
+      if (dbf) epilogue_fast<kForm, TLA_ACT_GELU, true>(p, m_base, n_base, lane, acc, region);
+      else epilogue_fast<kForm, TLA_ACT_GELU, false>(p, m_base, n_base, lane, acc, region);
       break;
     default:
-      if (dbf) epilogue_fast<kLds, TLA_ACT_NONE, true>(p, m_base, n_base, lane, acc, region);
-      else epilogue_fast<kLds, TLA_ACT_NONE, false>(p, m_base, n_base, lane, acc, region);
+      if (dbf) epilogue_fast<kForm, TLA_ACT_NONE, true>(p, m_base, n_base, lane, acc, region);
+      else epilogue_fast<kForm, TLA_ACT_NONE, false>(p, m_base, n_base, lane, acc, region);
       break;
   }
 }
@@ -598,19 +818,23 @@ __device__ __forceinline__ void epilogue_switch(const GemmParams& p, int m_base,
 // (the caller has synchronised the workgroup after its last LDS read), or
 // null.  A wave tile inside D whose C (if any) and bias (if any) have D's
 // 16-bit type takes the LDS path when C and D rows allow 16-byte vectors,
-// else the direct path with 8-byte vectors; anything else (edge tiles, fp32
-// or mixed-type C or bias, strided C or D) goes group by group through the
-// predicated epilogue4.
-template <int FM, int FN>
+// else the direct path with 8-byte vectors, else (kAny, row-major C and D
+// at even addresses, any pitch) the LDS path with realigned row accesses;
+// anything else (edge tiles, fp32 or mixed-type C or bias, column-major C
+// or D) goes group by group through the predicated epilogue4.
+template <int FM, int FN, bool kAny = false>
 __device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, int n_base, int lane,
                                                const f32x16 (&acc)[FM][FN], uint8_t* region) {
   const bool full = m_base + 32 * FM <= p.M && n_base + 32 * FN <= p.N;
   const bool b_ok = !p.bias || ((p.flags & kBiasVec) && p.bias_type == p.d_type);
   const bool c16 = p.c_type == p.d_type;
   if (full && b_ok && region && (p.flags & kD16) && (p.beta == 0.f || (c16 && (p.flags & kC16)))) {
-    epilogue_switch<true, FM, FN>(p, m_base, n_base, lane, acc, region);
+    epilogue_switch<1, FM, FN>(p, m_base, n_base, lane, acc, region);
   } else if (full && b_ok && (p.flags & kDVec) && (p.beta == 0.f || (c16 && (p.flags & kCVec)))) {
-    epilogue_switch<false, FM, FN>(p, m_base, n_base, lane, acc, region);
+    epilogue_switch<0, FM, FN>(p, m_base, n_base, lane, acc, region);
+  } else if (kAny && full && b_ok && region && (p.flags & kD2) &&
+             (p.beta == 0.f || (c16 && (p.flags & kC2)))) {
+    if constexpr (kAny) epilogue_switch<2, FM, FN>(p, m_base, n_base, lane, acc, region);
   } else {
     static_for<FM>([&](auto i) {
       const int m = m_base + 32 * i + mfma32_acc_col(lane, 0);

@@ -1,0 +1,270 @@
+// gemm_general.hip -- the four-wavefront GEMM kernel (2 x 2 waves of
+// (BM/2) x (BN/2), two LDS stages) for gfx950, in two forms:
+//
+//   register-staged  the general path: any order, pitch or alignment of A
+//                    and B, ragged K.  Each thread loads its chunks of the
+//                    next k-tile into registers before the MFMAs of the
+//                    current one and writes them to the other LDS stage
+//                    after them.  Elements outside the matrix load as zero.
+//                    Also the implicit-GEMM convolution's fallback loader.
+//   direct-to-LDS    e4m3 in the fast layout (variants 1 and 3).
+//
+//   D = act(alpha_eff * A.B + beta*C + bias),  fp32 accumulation.
+//
+// The tiling follows "CUTLASS / CuTe 主线" (hpc.payai.win/cutlass), section
+// 一: a workgroup owns a BM x BN block tile of D, each wavefront a quarter of
+// it, each 32x32 MFMA a 32x32 piece of that.  The epilogue is the shared
+// one of gemm_common.hpp.
+#include "gemm_common.hpp"
+
+namespace tla {
+namespace {
+
+// ------------------------------------------------------------------ kernel
+// kStages LDS stages of BM + BN rows of kRowBytes bytes each.  K-tile kt
+// lives in stage kt % kStages; up to kStages - 1 tiles are in flight, so the
+// copy of a tile has kStages - 1 tiles of matrix-core work to arrive in.
+//
+// Register-staged operand views (fixed per instantiation, so the loader
+// carries no stride it does not use): kAKC, A is K-contiguous (row-major),
+// else M-contiguous; kBView: B K-contiguous (kBK), N-contiguous through
+// element loads (kBN), or N-contiguous 16-bit with its slab as k rows of n
+// (RegSlabNT) read into fragments by transposing LDS reads (kBNT).
+enum : int { kBK = 0, kBN = 1, kBNT = 2 };
+
+template <int kCode, int BM, int BN, int kRowBytes, int kStages, bool kFast, bool kConv = false,
+          bool kAKC = true, int kBView = kBK>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
+  constexpr bool kNT = kBView == kBNT;
+  using Atom = MfmaAtom<kCode>;
+  using Frag = typename Atom::Frag;
+  constexpr int EB = elem_bytes(kCode);
+  constexpr int BK = kRowBytes / EB;         // K elements per k-tile
+  constexpr int WM = BM / 2, WN = BN / 2;    // 2 x 2 wavefronts
+  constexpr int FM = WM / 32, FN = WN / 32;  // MFMA tiles per wave
+  constexpr int KSTEPS = BK / Atom::kK;
+  static_assert(KSTEPS >= 1 && BK % Atom::kK == 0, "slab narrower than one MFMA step");
+  constexpr int SLAB_A = BM * kRowBytes, STAGE = (BM + BN) * kRowBytes;
+  static_assert(kStages * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(!kNT || (EB == 2 && Atom::kK == 16 && !kFast && !kConv),
+                "N-contiguous B slab: 16-bit operands, register-staged path");
+  static_assert(!(kFast || kConv) || (kAKC && kBView == kBK), "K-contiguous operands");
+  // global_load_lds instructions one thread issues per k-tile
+  constexpr int kLoadsPerTile = (BM + BN) * kRowBytes / 16 / kThreads;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tm, tn;
+  schedule(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm0 = (wave & 1) * WM, wn0 = (wave >> 1) * WN;
+
+  f32x16 acc[FM][FN];
+  static_for<FM>([&](auto i) { static_for<FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
+
+  // Fragment double buffer and the pieces of one MFMA k-step.
+  Frag a[2][FM], b[2][FN];
+  auto read_frags = [&](auto buf, const uint8_t* stage, auto ks) {
+    static_for<FM>([&](auto i) {
+      a[buf][i] = load_frag<kCode, kRowBytes>(stage, wm0 + 32 * i + (lane & 31), ks, lane);
+    });
+    static_for<FN>([&](auto j) {
+      if constexpr (kNT)
+        b[buf][j] = load_frag_nt<2 * BN>(stage + SLAB_A, wn0 + 32 * j, ks, lane);
+      else
+        b[buf][j] = load_frag<kCode, kRowBytes>(stage + SLAB_A, wn0 + 32 * j + (lane & 31), ks,
+                                                lane);
+    });
+  };
+  // MFMAs number lo .. hi-1 of a step (i major, j minor)
+  auto mfmas = [&](auto buf, auto lo, auto hi) {
+    static_for<hi - lo>([&](auto q) {
+      constexpr int idx = lo + q;
+      Atom::mma(acc[idx / FN][idx % FN], b[buf][idx % FN], a[buf][idx / FN]);
+    });
+  };
+  constexpr int kReads = (FM + FN) * (Atom::kLaneBytes / 16);
+  constexpr int kMfmas = FM * FN;
+
+  const int KT = (p.K + BK - 1) / BK;
+  if constexpr (kFast) {
+    // One software pipeline over all k-steps.  The fragments of step g+1 are
+    // read at the start of step g, a whole step of MFMAs before use.  In the
+    // last step of k-tile kt, half-way through its MFMAs, every wave waits
+    // for tile kt+1 and meets at a barrier; that barrier also proves every
+    // wave is done reading tile kt's stage, which is refilled at once with
+    // tile kt+kStages.
+    static_assert(KSTEPS % 2 == 0, "fragment buffers alternate per step");
+    const int64_t a_rb = p.a_sr * EB, b_rb = p.b_sr * EB;
+    auto issue = [&](int kt) {
+      uint8_t* st = smem + (kt % kStages) * STAGE;
+      const int64_t kb = (int64_t)kt * kRowBytes;
+      dma_slab<BM, kRowBytes>(p.A, a_rb, m0, p.M, kb, st, tid);
+      dma_slab<BN, kRowBytes>(p.B, b_rb, n0, p.N, kb, st + SLAB_A, tid);
+    };
+    // wait until tile `t` has landed, given tiles up to `last_issued` were issued
+    auto wait_tile = [&](int t, int last_issued) {
+      const int after = min(kStages - 1, last_issued - t);
+      static_for<kStages>([&](auto n) {
+        if (after == n) wait_vmcnt<n * kLoadsPerTile>();
+      });
+    };
+    static_for<kStages>([&](auto s) {
+      if (s < KT) issue(s);
+    });
+    if (KT > 0) {
+      wait_tile(0, min(kStages, KT) - 1);
+      __syncthreads();
+      read_frags(std::integral_constant<int, 0>{}, smem, std::integral_constant<int, 0>{});
+    }
+    for (int kt = 0; kt < KT; ++kt) {
+      const uint8_t* stage = smem + (kt % kStages) * STAGE;
+      static_for<KSTEPS>([&](auto ks) {
+        constexpr int cur = ks & 1;
+        if constexpr (ks + 1 < KSTEPS) {
+          read_frags(std::integral_constant<int, cur ^ 1>{}, stage,
+                     std::integral_constant<int, ks + 1>{});
+          mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
+                std::integral_constant<int, kMfmas>{});
+          __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, kMfmas, 0);
+        } else {
+          mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
+                std::integral_constant<int, kMfmas / 2>{});
+          if (kt + 1 < KT) {
+            // tiles issued so far: 0 .. min(kt + kStages - 1, KT - 1)
+            wait_tile(kt + 1, min(kt + kStages - 1, KT - 1));
+            __syncthreads();
+            if (kt + kStages < KT) issue(kt + kStages);
+            read_frags(std::integral_constant<int, cur ^ 1>{},
+                       smem + ((kt + 1) % kStages) * STAGE, std::integral_constant<int, 0>{});
+          }
+          mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, kMfmas / 2>{},
+                std::integral_constant<int, kMfmas>{});
+        }
+      });
+    }
+  } else {
+    static_assert(kStages == 2, "register-staged path double-buffers");
+    // k-steps of one tile from LDS, fragments of step ks+1 read during ks
+    auto compute = [&](const uint8_t* stage) {
+      read_frags(std::integral_constant<int, 0>{}, stage, std::integral_constant<int, 0>{});
+      static_for<KSTEPS>([&](auto ks) {
+        constexpr int cur = ks & 1;
+        if constexpr (ks + 1 < KSTEPS)
+          read_frags(std::integral_constant<int, cur ^ 1>{}, stage,
+                     std::integral_constant<int, ks + 1>{});
+        mfmas(std::integral_constant<int, cur>{}, std::integral_constant<int, 0>{},
+              std::integral_constant<int, kMfmas>{});
+      });
+    };
+    static_assert(!kConv || !kFast, "the convolution view uses the register-staged path");
+    std::conditional_t<kConv, ConvSlab<BM, EB, kRowBytes>, RegSlab<BM, EB, kRowBytes, kAKC>> ra;
+    std::conditional_t<kNT, RegSlabNT<BN, BK>, RegSlab<BN, EB, kRowBytes, kBView == kBK>> rb;
+    const bool a_vec = (p.flags >> 8) & 1, b_vec = (p.flags >> 9) & 1;
+    const int64_t a_s = kAKC ? p.a_sr : p.a_sk;  // the stride that is not 1
+    const int64_t b_s = kBView == kBK ? p.b_sr : p.b_sk;
+    auto load = [&](int k0) {
+      if constexpr (kConv) ra.load_conv(p, m0, k0, a_vec, tid);
+      else ra.load(p.A, a_s, m0, p.M, k0, p.K, a_vec, tid);
+      if constexpr (kNT) rb.load(p.B, b_s, n0, p.N, k0, p.K, b_vec, tid);
+      else rb.load(p.B, b_s, n0, p.N, k0, p.K, b_vec, tid);
+    };
+    auto store = [&](uint8_t* st) {
+      ra.store(st, !kConv && !a_vec, tid);
+      rb.store(st + SLAB_A, !b_vec, tid);
+    };
+    if (KT > 0) {
+      load(0);
+      store(smem);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      uint8_t* cur = smem + (kt & 1) * STAGE;
+      uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
+      if (kt + 1 < KT) load((kt + 1) * BK);
+      compute(cur);
+      if (kt + 1 < KT) store(nxt);
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: acc[i][j] holds the D^T piece for rows m0+wm0+32i.. and
+  // columns n0+wn0+32j..; value r of lane l sits at (row, col) =
+  // (lane%32, mfma32_acc_row(l, r)) of that 32x32 piece.  No copy is in
+  // flight here; after the barrier the stages are the waves' regions.
+  constexpr bool kLdsEpi = 4 * WM * 64 * FN <= kStages * STAGE;
+  __syncthreads();
+  epilogue_tiles<FM, FN, !kFast>(p, m0 + wm0, n0 + wn0, lane, acc,
+                         kLdsEpi ? smem + wave * WM * 64 * FN : nullptr);
+}
+
+
+template <int kCode, int BM, int BN, bool kFast, bool kConv, bool kAKC, int kBView>
+int launch(const GemmParams& p0, hipStream_t stream) {
+  GemmParams p = p0;
+  int64_t grid;
+  set_grid(p, BM, BN, &grid);
+  if (grid <= 0) return TLA_OK;
+  if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((gemm_kernel<kCode, BM, BN, 128, 2, kFast, kConv, kAKC, kBView>),
+                     dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
+}
+
+// The register-staged kernel for the operand views p's strides describe
+// (A: a_sk == 1 K-contiguous, else M-contiguous; B: b_sk == 1 K-contiguous,
+// else N-contiguous, which 16-bit operands take through the k-rows-of-n
+// slab).  3001 x 4097 x 777 fp16 with A and B row-major at odd pitches:
+// 167 us with B's slab as k rows of n, 738 us with n rows of k filled element
+// by element.
+template <int kCode>
+int launch_views(const GemmParams& p, hipStream_t s) {
+  constexpr int kBNc = kCode == kE4M3 ? kBN : kBNT;
+  const bool akc = p.a_sk == 1, bkc = p.b_sk == 1;
+  if (akc)
+    return bkc ? launch<kCode, 128, 128, false, false, true, kBK>(p, s)
+               : launch<kCode, 128, 128, false, false, true, kBNc>(p, s);
+  return bkc ? launch<kCode, 128, 128, false, false, false, kBK>(p, s)
+             : launch<kCode, 128, 128, false, false, false, kBNc>(p, s);
+}
+
+}  // namespace
+
+int launch_general(const GemmParams& p, int type, hipStream_t stream) {
+  switch (type) {
+    case kBF16: return launch_views<kBF16>(p, stream);
+    case kF16: return launch_views<kF16>(p, stream);
+    case kE4M3: return launch_views<kE4M3>(p, stream);
+    default: return TLA_ERR_UNSUPPORTED;
+  }
+}
+
+int launch_two_stage_e4m3(const GemmParams& p, bool big, hipStream_t stream) {
+  return big ? launch<kE4M3, 256, 256, true, false, true, kBK>(p, stream)
+             : launch<kE4M3, 128, 128, true, false, true, kBK>(p, stream);
+}
+
+int launch_conv_general(const GemmParams& p, int type, hipStream_t stream) {
+  switch (type) {
+    case kBF16: return launch<kBF16, 128, 128, false, true, true, kBK>(p, stream);
+    case kF16: return launch<kF16, 128, 128, false, true, true, kBK>(p, stream);
+    default: return TLA_ERR_UNSUPPORTED;
+  }
+}
+
+const void* general_kernel(int type) {
+  switch (type) {
+    case kBF16: return (const void*)gemm_kernel<kBF16, 128, 128, 128, 2, false>;
+    case kF16: return (const void*)gemm_kernel<kF16, 128, 128, 128, 2, false>;
+    case kE4M3: return (const void*)gemm_kernel<kE4M3, 128, 128, 128, 2, false>;
+    default: return nullptr;
+  }
+}
+
+const void* two_stage_e4m3_kernel(bool big) {
+  return big ? (const void*)gemm_kernel<kE4M3, 256, 256, 128, 2, true>
+             : (const void*)gemm_kernel<kE4M3, 128, 128, 128, 2, true>;
+}
+
+}  // namespace tla
