@@ -210,74 +210,107 @@ __device__ __forceinline__ i32x4 realign16(const i32x4& lo, uint32_t hi, uint32_
   return r;
 }
 
-// Element-predicated, register-staged slab copy of an operand view
-// (row, k) -> row*s_r + k*s_k, fixed at compile time to one of the two
-// views the library builds: kKC (K-contiguous, s_k = 1) or row-contiguous
-// (s_r = 1, an M- or N-contiguous matrix).  K-contiguous views use the
-// row-contiguous thread map (consecutive lanes walk K) and move whole
-// 16-byte chunks -- one 16-byte load when the rows are 16-byte aligned, the
-// dword-aligned pair of load16_split otherwise (shifted into place by
-// store) -- and only the chunk that crosses K element by element; the
-// others use the column-major variant (consecutive lanes walk rows, so each
-// element load coalesces) and move every chunk element by element.  Rows
-// past rows_valid and elements past K load as zero.
+// kCE = 16 / EB elements e = 0 .. kCE - 1 of a line, element e at
+// p + min(i + e, last) * step: the ones with i + e < lim as loaded, the
+// others zero.  Every address is clamped to element `last`, so all loads are
+// issued unconditionally and stay inside the matrix.
+template <int EB>
+__device__ __forceinline__ i32x4 gather16(const uint8_t* p, int64_t step, int i, int lim,
+                                          int last) {
+  constexpr int kCE = 16 / EB;
+  uint8_t bytes[16];
+#pragma unroll
+  for (int e = 0; e < kCE; ++e) {
+    const uint8_t* q = p + (int64_t)min(i + e, last) * step;
+    const bool ok = i + e < lim;
+#pragma unroll
+    for (int b = 0; b < EB; ++b) {
+      const uint8_t x = q[b];
+      bytes[e * EB + b] = ok ? x : 0;
+    }
+  }
+  return __builtin_bit_cast(i32x4, bytes);
+}
+
+// Register-staged slab copy of an operand view (row, k) -> row*s_r +
+// k*s_k, fixed at compile time to one of the two views the library builds:
+// kKC (K-contiguous, s_k = 1) or row-contiguous (s_r = 1, an M- or
+// N-contiguous matrix).  K-contiguous views use the row-contiguous thread
+// map (consecutive lanes walk K) and move a tile inside K as whole 16-byte
+// chunks through load16_split (load_whole), shifted into place by store();
+// the last, ragged tile (load_edge) moves its chunks inside K the same way
+// and the one that crosses K element by element, and the other view (the
+// column-major map: consecutive lanes walk rows, so each element load
+// coalesces) goes element by element.  Elements past K load as zero; rows
+// past rows_valid repeat the last row (their products land in rows or
+// columns of D that are never stored).  load_whole has no per-lane branch,
+// so its loads stay in flight until store().
 template <int ROWS, int EB, int kRowBytes, bool kKC>
 struct RegSlab {
   using Swz = typename Slab<kRowBytes>::Swz;
   static constexpr int kChunks = Slab<kRowBytes>::kChunks;
   static constexpr int kI = ROWS * kChunks / kThreads;
   static constexpr int kCE = 16 / EB;  // elements per 16-byte chunk
+  static constexpr int kTileK = kChunks * kCE;
   static_assert(kI <= 8, "byte shifts pack 4 bits per chunk");
   i32x4 v[kI];
   uint32_t hi[kI];
   uint32_t shifts;  // byte shift of chunk it in bits 4 it .. 4 it + 1
 
-  // s: the row stride (kKC) or the k stride (otherwise), in elements
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t s, int row0,
-                                       int rows_valid, int k0, int K, bool vec_ok, int tid) {
-    constexpr StripMinedMap map(ROWS, kChunks, kThreads, 1, kI, kKC ? 1 : 0);
-    static_assert(map.well_formed(), "slab thread map");
+  static constexpr StripMinedMap map() {
+    return StripMinedMap(ROWS, kChunks, kThreads, 1, kI, kKC ? 1 : 0);
+  }
+
+  // k0 .. k0 + kTileK - 1 inside K; s: the row stride in elements
+  __device__ __forceinline__ void load_whole(const uint8_t* __restrict__ base, int64_t s, int row0,
+                                             int rows_valid, int k0, int tid) {
+    static_assert(kKC, "whole chunks along K");
+    constexpr StripMinedMap m = map();
+    static_assert(m.well_formed(), "slab thread map");
     shifts = 0;
 #pragma unroll
     for (int it = 0; it < kI; ++it) {
-      const int gr = row0 + map.row(tid, it, 0);
-      const int gk = k0 + map.col(tid, it, 0) * kCE;
+      const int gr = min(row0 + m.row(tid, it, 0), rows_valid - 1);
+      const uint8_t* p = base + (gr * s + (int64_t)(k0 + m.col(tid, it, 0) * kCE)) * EB;
+      shifts |= load16_split(p, v[it], hi[it]) << (4 * it);
+    }
+  }
+
+  // s: the row stride (kKC) or the k stride (otherwise), in elements.
+  // Chunks past K are zero without a load; a K-contiguous chunk inside K
+  // moves whole, the one that crosses K (and every chunk of the other view)
+  // element by element.
+  __device__ __forceinline__ void load_edge(const uint8_t* __restrict__ base, int64_t s, int row0,
+                                            int rows_valid, int k0, int K, int tid) {
+    constexpr StripMinedMap m = map();
+    static_assert(m.well_formed(), "slab thread map");
+    shifts = 0;
+#pragma unroll
+    for (int it = 0; it < kI; ++it) {
+      const int gr = min(row0 + m.row(tid, it, 0), rows_valid - 1);
+      const int gk = k0 + m.col(tid, it, 0) * kCE;
+      const int64_t s_r = kKC ? s : 1, s_k = kKC ? 1 : s;
+      const uint8_t* row = base + gr * s_r * EB;
       i32x4 x = {0, 0, 0, 0};
       uint32_t h = 0;
-      if (gr < rows_valid) {
-        const int64_t s_r = kKC ? s : 1, s_k = kKC ? 1 : s;
-        const uint8_t* p = base + (gr * s_r + (int64_t)gk * s_k) * EB;
-        if (kKC && gk + kCE <= K) {
-          if (vec_ok)
-            x = *(const i32x4*)p;
-          else
-            shifts |= load16_split(p, x, h) << (4 * it);
-        } else {
-          uint8_t bytes[16] = {};
-#pragma unroll
-          for (int e = 0; e < kCE; ++e) {
-            if (gk + e < K) {
-              const uint8_t* q = p + (int64_t)e * s_k * EB;
-#pragma unroll
-              for (int b = 0; b < EB; ++b) bytes[e * EB + b] = q[b];
-            }
-          }
-          x = __builtin_bit_cast(i32x4, bytes);
-        }
+      if (gk < K) {
+        if (kKC && gk + kCE <= K)
+          shifts |= load16_split(row + (int64_t)gk * EB, x, h) << (4 * it);
+        else
+          x = gather16<EB>(row, s_k * EB, gk, K, K - 1);
       }
       v[it] = x;
       hi[it] = h;
     }
   }
 
-  // realign: some chunks came through load16_split (rows not 16-byte aligned)
-  __device__ __forceinline__ void store(uint8_t* slab, bool realign, int tid) const {
-    constexpr StripMinedMap map(ROWS, kChunks, kThreads, 1, kI, kKC ? 1 : 0);
+  __device__ __forceinline__ void store(uint8_t* slab, int tid) const {
+    constexpr StripMinedMap m = map();
 #pragma unroll
     for (int it = 0; it < kI; ++it) {
-      const int r = map.row(tid, it, 0), c = map.col(tid, it, 0);
+      const int r = m.row(tid, it, 0), c = m.col(tid, it, 0);
       *(i32x4*)(slab + r * kRowBytes + Swz::chunk(r, c) * 16) =
-          (kKC && realign) ? realign16(v[it], hi[it], shifts >> (4 * it)) : v[it];
+          kKC ? realign16(v[it], hi[it], shifts >> (4 * it)) : v[it];
     }
   }
 };
@@ -287,9 +320,9 @@ struct RegSlab {
 // n (2 BN bytes; 16-byte chunk c of row r stored at chunk c ^ 4 (r % 4)),
 // and load_frag_nt reads it back with ds_read_b64_tr_b16.  Consecutive
 // lanes walk the chunks of one k row, so a load instruction covers runs of
-// whole rows; full chunks move as 16 bytes (one load on 16-byte aligned
-// rows, load16_split otherwise), the chunk that crosses N element by element,
-// and rows past K and columns past N load as zero.
+// whole rows; tiles inside K and N move whole chunks through load16_split
+// (load_whole), edge tiles element by element with rows past K and columns
+// past N zero (load_edge).
 template <int BN, int BK>
 struct RegSlabNT {
   static constexpr int kRow = 2 * BN;
@@ -302,8 +335,22 @@ struct RegSlabNT {
   uint32_t hi[kI];
   uint32_t shifts;  // byte shift of chunk it in bits 4 it .. 4 it + 1
 
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t ld, int n0, int N,
-                                       int k0, int K, bool vec_ok, int tid) {
+  // k0 .. k0 + BK - 1 inside K and n0 .. n0 + BN - 1 inside N
+  __device__ __forceinline__ void load_whole(const uint8_t* __restrict__ base, int64_t ld, int n0,
+                                             int k0, int tid) {
+    shifts = 0;
+#pragma unroll
+    for (int it = 0; it < kI; ++it) {
+      const int sc = tid + kThreads * it, r = sc / kCh, c = sc % kCh;
+      const uint8_t* p = base + ((int64_t)(k0 + r) * ld + n0 + 8 * c) * 2;
+      shifts |= load16_split(p, v[it], hi[it]) << (4 * it);
+    }
+  }
+
+  // Chunks past K or N are zero without a load, chunks inside both move
+  // whole, the chunk that crosses N element by element.
+  __device__ __forceinline__ void load_edge(const uint8_t* __restrict__ base, int64_t ld, int n0,
+                                            int N, int k0, int K, int tid) {
     shifts = 0;
 #pragma unroll
     for (int it = 0; it < kI; ++it) {
@@ -312,36 +359,23 @@ struct RegSlabNT {
       i32x4 x = {0, 0, 0, 0};
       uint32_t h = 0;
       if (gk < K && gn < N) {
-        const uint8_t* p = base + ((int64_t)gk * ld + gn) * 2;
-        if (gn + 8 <= N) {
-          if (vec_ok)
-            x = *(const i32x4*)p;
-          else
-            shifts |= load16_split(p, x, h) << (4 * it);
-        } else {
-          uint8_t bytes[16] = {};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (gn + e < N) {
-              bytes[2 * e] = p[2 * e];
-              bytes[2 * e + 1] = p[2 * e + 1];
-            }
-          }
-          x = __builtin_bit_cast(i32x4, bytes);
-        }
+        const uint8_t* row = base + (int64_t)gk * ld * 2;
+        if (gn + 8 <= N)
+          shifts |= load16_split(row + (int64_t)gn * 2, x, h) << (4 * it);
+        else
+          x = gather16<2>(row, 2, gn, N, N - 1);
       }
       v[it] = x;
       hi[it] = h;
     }
   }
 
-  // realign: some chunks came through load16_split (rows not 16-byte aligned)
-  __device__ __forceinline__ void store(uint8_t* slab, bool realign, int tid) const {
+  __device__ __forceinline__ void store(uint8_t* slab, int tid) const {
 #pragma unroll
     for (int it = 0; it < kI; ++it) {
       const int sc = tid + kThreads * it, r = sc / kCh, c = sc % kCh;
       *(i32x4*)(slab + r * kRow + (c ^ (4 * (r & 3))) * 16) =
-          realign ? realign16(v[it], hi[it], shifts >> (4 * it)) : v[it];
+          realign16(v[it], hi[it], shifts >> (4 * it));
     }
   }
 };
@@ -397,6 +431,7 @@ struct ConvSlab : RegSlab<ROWS, EB, kRowBytes, true> {
     constexpr StripMinedMap kmap(ROWS, Base::kChunks, kThreads, 1, Base::kI, 1);
     constexpr int kCE = Base::kCE;
     const int PQ = p.cP * p.cQ;
+    this->shifts = 0;  // whole chunks are loaded aligned or element by element
 #pragma unroll
     for (int it = 0; it < Base::kI; ++it) {
       const int m = row0 + kmap.row(tid, it, 0);
@@ -424,6 +459,7 @@ struct ConvSlab : RegSlab<ROWS, EB, kRowBytes, true> {
         }
       }
       this->v[it] = x;
+      this->hi[it] = 0;
     }
   }
 };

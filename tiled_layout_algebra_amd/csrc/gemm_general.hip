@@ -159,34 +159,64 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
       });
     };
     static_assert(!kConv || !kFast, "the convolution view uses the register-staged path");
+    // Tile kt + 1 is loaded into registers before the MFMAs of tile kt and
+    // written to the other LDS stage after them.  Tiles 0 .. KTw - 1 lie
+    // inside K (and, for the k-rows-of-n B slab, inside N): the main loop
+    // loads only those, whole chunks without a per-lane branch, so their
+    // loads stay in flight across the MFMAs; the ragged rest goes through a
+    // loop of its own with the element-wise loader.
     std::conditional_t<kConv, ConvSlab<BM, EB, kRowBytes>, RegSlab<BM, EB, kRowBytes, kAKC>> ra;
     std::conditional_t<kNT, RegSlabNT<BN, BK>, RegSlab<BN, EB, kRowBytes, kBView == kBK>> rb;
-    const bool a_vec = (p.flags >> 8) & 1, b_vec = (p.flags >> 9) & 1;
+    const bool a_vec = (p.flags >> 8) & 1;
     const int64_t a_s = kAKC ? p.a_sr : p.a_sk;  // the stride that is not 1
     const int64_t b_s = kBView == kBK ? p.b_sr : p.b_sk;
-    auto load = [&](int k0) {
-      if constexpr (kConv) ra.load_conv(p, m0, k0, a_vec, tid);
-      else ra.load(p.A, a_s, m0, p.M, k0, p.K, a_vec, tid);
-      if constexpr (kNT) rb.load(p.B, b_s, n0, p.N, k0, p.K, b_vec, tid);
-      else rb.load(p.B, b_s, n0, p.N, k0, p.K, b_vec, tid);
+    auto load = [&](int k0, auto whole) {
+      if constexpr (kConv) {
+        ra.load_conv(p, m0, k0, a_vec, tid);
+      } else {
+        if constexpr (whole && kAKC) ra.load_whole(p.A, a_s, m0, p.M, k0, tid);
+        else ra.load_edge(p.A, a_s, m0, p.M, k0, p.K, tid);
+      }
+      if constexpr (kNT) {
+        if constexpr (whole) rb.load_whole(p.B, b_s, n0, k0, tid);
+        else rb.load_edge(p.B, b_s, n0, p.N, k0, p.K, tid);
+      } else {
+        if constexpr (whole && kBView == kBK) rb.load_whole(p.B, b_s, n0, p.N, k0, tid);
+        else rb.load_edge(p.B, b_s, n0, p.N, k0, p.K, tid);
+      }
     };
     auto store = [&](uint8_t* st) {
-      ra.store(st, !kConv && !a_vec, tid);
-      rb.store(st + SLAB_A, !b_vec, tid);
+      ra.store(st, tid);
+      rb.store(st + SLAB_A, tid);
     };
+    using Whole = std::true_type;
+    using Edge = std::false_type;
+    const int KTw = (kNT && n0 + BN > p.N) ? 0 : p.K / BK;
     if (KT > 0) {
-      load(0);
+      if (KTw > 0) load(0, Whole{});
+      else load(0, Edge{});
       store(smem);
     }
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
+    // tile kt from its stage; mode 1 / 2 loads tile kt + 1 whole / element-wise
+    auto iter = [&](int kt, auto mode) {
       uint8_t* cur = smem + (kt & 1) * STAGE;
       uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
-      if (kt + 1 < KT) load((kt + 1) * BK);
+      if constexpr (mode == 1) load((kt + 1) * BK, Whole{});
+      if constexpr (mode == 2) load((kt + 1) * BK, Edge{});
+      // the loads go out before the MFMAs and the LDS writes (which wait for
+      // them) after the last one: the scheduler would otherwise sink the
+      // loads and hoist the writes into the MFMA sequence
+      if constexpr (mode != 0) __builtin_amdgcn_sched_barrier(0);
       compute(cur);
-      if (kt + 1 < KT) store(nxt);
+      if constexpr (mode != 0) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (mode != 0) store(nxt);
       __syncthreads();
-    }
+    };
+    int kt = 0;
+    for (; kt + 1 < KTw; ++kt) iter(kt, std::integral_constant<int, 1>{});
+    for (; kt + 1 < KT; ++kt) iter(kt, std::integral_constant<int, 2>{});
+    if (kt < KT) iter(kt, std::integral_constant<int, 0>{});
   }
 
   // Epilogue: acc[i][j] holds the D^T piece for rows m0+wm0+32i.. and
