@@ -198,6 +198,7 @@ CSRC = os.path.join(ROOT, "tiled_layout_algebra_amd", "csrc")
 _HEADERS = ["tla/layout.hpp", "tla/copy.hpp", "tla/mfma.hpp", "kernels.hpp"]
 # the sources each measured kernel is built from, besides _HEADERS
 GEMM_SOURCES = "gemm_pingpong.hip+gemm_common.hpp"
+GENERAL_SOURCES = "gemm_general.hip+gemm_common.hpp"
 TRANSPOSE_SOURCES = "transpose.hip"
 
 
@@ -328,9 +329,10 @@ def gemm_call(tla, case, dA, dB, dD, dC, dbias, stream):
     return run
 
 
-def extra_gemm(tla, W, case, peak, stream, warmup, steps, cpu_s):
+def extra_gemm(tla, W, case, peak, stream, warmup, steps, cpu_s, label=None, sources=None):
     """One of the other measured GEMMs, timed on its own after the step loop:
-    TFLOP/s against `peak`, and (cpu_s > 0) the oracle on a row sample."""
+    TFLOP/s against `peak`, and (cpu_s > 0) the oracle on a row sample;
+    `label` names the kernel's row in profiles/kernel_counters.txt."""
     import torch
     from workloads.device import to_dev
     inp = W.gemm_inputs(case)
@@ -341,7 +343,6 @@ def extra_gemm(tla, W, case, peak, stream, warmup, steps, cpu_s):
     run = gemm_call(tla, case, dA, dB, dD, dC, dbias, stream)
     t = time_launches(run, stream, warmup, steps)
     tf = case.flops() / t.mean() / 1e12
-    label = {W.E4M3: "gemm_pingpong_kernel<e4m3>"}.get(case.a_type)
     out = {"workload": case.name, "variant": tla.gemm_variant(
                case.M, case.N, case.K, dA, case.a_type, case.a_order, case.lda, dB, case.b_type,
                case.b_order, case.ldb, dD, case.d_type, case.d_order, case.ldd, C=dC,
@@ -350,7 +351,7 @@ def extra_gemm(tla, W, case, peak, stream, warmup, steps, cpu_s):
                act=case.act),
            "value": round(tf, 2), "unit": "TFLOP/s",
            "roofline": roofline(tf, peak, "mfma", "TFLOP/s", t,
-                                kernel_counters(label, GEMM_SOURCES) if label else None)}
+                                kernel_counters(label, sources) if label else None)}
     if cpu_s > 0:
         out["cpu_baseline"] = cpu_baseline(case, inp, cpu_s)
     del dA, dB, dC, dbias, dD
@@ -527,9 +528,10 @@ def main():
     if not args.no_extra:
         cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds / 3
         out["fp8"] = extra_gemm(tla, W, W.GEMM_E4M3_8192, PEAK_FP8_TFLOPS, stream, args.warmup,
-                                K, cpu_s)
+                                K, cpu_s, "gemm_pingpong_kernel<e4m3>", GEMM_SOURCES)
         out["f16_ragged"] = extra_gemm(tla, W, W.GEMM_F16_RAGGED, PEAK_BF16_TFLOPS, stream,
-                                       args.warmup, K, cpu_s / 2)
+                                       args.warmup, K, cpu_s / 2, "gemm_kernel<f16,nt>",
+                                       GENERAL_SOURCES)
         out["f16_256"] = extra_gemm(tla, W, W.GEMM_F16_256, PEAK_BF16_TFLOPS, stream,
                                     args.warmup, K, 0.0)
     if not args.no_cpu_baseline:
