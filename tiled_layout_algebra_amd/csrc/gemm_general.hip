@@ -32,9 +32,14 @@ namespace {
 // (RegSlabNT) read into fragments by transposing LDS reads (kBNT).
 enum : int { kBK = 0, kBN = 1, kBNT = 2 };
 
+// The register-staged form with K-contiguous or k-rows-of-n operands asks
+// for two waves per SIMD (at most 256 VGPRs): left to itself the compiler
+// let its two register sets push the kernel to 260-316 VGPRs, one wave per
+// SIMD.  With an element-wise view it would spill, so those keep one.
 template <int kCode, int BM, int BN, int kRowBytes, int kStages, bool kFast, bool kConv = false,
           bool kAKC = true, int kBView = kBK>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
+__global__ __launch_bounds__(kThreads, (kFast || !kAKC || kBView == kBN) ? 1 : 2) void gemm_kernel(
+    const GemmParams p) {
   constexpr bool kNT = kBView == kBNT;
   using Atom = MfmaAtom<kCode>;
   using Frag = typename Atom::Frag;
@@ -159,64 +164,86 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmParams p) {
       });
     };
     static_assert(!kConv || !kFast, "the convolution view uses the register-staged path");
-    // Tile kt + 1 is loaded into registers before the MFMAs of tile kt and
-    // written to the other LDS stage after them.  Tiles 0 .. KTw - 1 lie
-    // inside K (and, for the k-rows-of-n B slab, inside N): the main loop
-    // loads only those, whole chunks without a per-lane branch, so their
-    // loads stay in flight across the MFMAs; the ragged rest goes through a
-    // loop of its own with the element-wise loader.
-    std::conditional_t<kConv, ConvSlab<BM, EB, kRowBytes>, RegSlab<BM, EB, kRowBytes, kAKC>> ra;
-    std::conditional_t<kNT, RegSlabNT<BN, BK>, RegSlab<BN, EB, kRowBytes, kBView == kBK>> rb;
+    // Two register sets per operand.  Tiles 0 .. KTw - 1 lie inside K (and,
+    // for the k-rows-of-n B slab, inside N); they load as whole chunks with
+    // no per-lane branch, two tiles ahead: tile t + 2 goes into set t % 2
+    // before the MFMAs of tile t, and set (t + 1) % 2 (tile t + 1, loaded a
+    // whole iteration earlier) is written to the other LDS stage after them.
+    // The ragged rest goes one tile ahead through the element-wise loader.
+    // Tile t lives in LDS stage t % 2.
+    using RA = std::conditional_t<kConv, ConvSlab<BM, EB, kRowBytes>, RegSlab<BM, EB, kRowBytes, kAKC>>;
+    using RB = std::conditional_t<kNT, RegSlabNT<BN, BK>, RegSlab<BN, EB, kRowBytes, kBView == kBK>>;
+    RA ra[2];
+    RB rb[2];
     const bool a_vec = (p.flags >> 8) & 1;
     const int64_t a_s = kAKC ? p.a_sr : p.a_sk;  // the stride that is not 1
     const int64_t b_s = kBView == kBK ? p.b_sr : p.b_sk;
-    auto load = [&](int k0, auto whole) {
+    auto load = [&](int k0, auto whole, auto set) {
       if constexpr (kConv) {
-        ra.load_conv(p, m0, k0, a_vec, tid);
+        ra[set].load_conv(p, m0, k0, a_vec, tid);
       } else {
-        if constexpr (whole && kAKC) ra.load_whole(p.A, a_s, m0, p.M, k0, tid);
-        else ra.load_edge(p.A, a_s, m0, p.M, k0, p.K, tid);
+        if constexpr (whole && kAKC) ra[set].load_whole(p.A, a_s, m0, p.M, k0, tid);
+        else ra[set].load_edge(p.A, a_s, m0, p.M, k0, p.K, tid);
       }
       if constexpr (kNT) {
-        if constexpr (whole) rb.load_whole(p.B, b_s, n0, k0, tid);
-        else rb.load_edge(p.B, b_s, n0, p.N, k0, p.K, tid);
+        if constexpr (whole) rb[set].load_whole(p.B, b_s, n0, k0, tid);
+        else rb[set].load_edge(p.B, b_s, n0, p.N, k0, p.K, tid);
       } else {
-        if constexpr (whole && kBView == kBK) rb.load_whole(p.B, b_s, n0, p.N, k0, tid);
-        else rb.load_edge(p.B, b_s, n0, p.N, k0, p.K, tid);
+        if constexpr (whole && kBView == kBK) rb[set].load_whole(p.B, b_s, n0, p.N, k0, tid);
+        else rb[set].load_edge(p.B, b_s, n0, p.N, k0, p.K, tid);
       }
     };
-    auto store = [&](uint8_t* st) {
-      ra.store(st, tid);
-      rb.store(st + SLAB_A, tid);
+    auto store = [&](uint8_t* st, auto set) {
+      ra[set].store(st, tid);
+      rb[set].store(st + SLAB_A, tid);
     };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
     using Whole = std::true_type;
     using Edge = std::false_type;
     const int KTw = (kNT && n0 + BN > p.N) ? 0 : p.K / BK;
     if (KT > 0) {
-      if (KTw > 0) load(0, Whole{});
-      else load(0, Edge{});
-      store(smem);
+      if (KTw > 0) load(0, Whole{}, S0{});
+      else load(0, Edge{}, S0{});
+      store(smem, S0{});
+      if (KTw > 1) load(BK, Whole{}, S1{});
     }
     __syncthreads();
-    // tile kt from its stage; mode 1 / 2 loads tile kt + 1 whole / element-wise
-    auto iter = [&](int kt, auto mode) {
-      uint8_t* cur = smem + (kt & 1) * STAGE;
-      uint8_t* nxt = smem + ((kt + 1) & 1) * STAGE;
-      if constexpr (mode == 1) load((kt + 1) * BK, Whole{});
-      if constexpr (mode == 2) load((kt + 1) * BK, Edge{});
-      // the loads go out before the MFMAs and the LDS writes (which wait for
-      // them) after the last one: the scheduler would otherwise sink the
-      // loads and hoist the writes into the MFMA sequence
-      if constexpr (mode != 0) __builtin_amdgcn_sched_barrier(0);
-      compute(cur);
-      if constexpr (mode != 0) __builtin_amdgcn_sched_barrier(0);
-      if constexpr (mode != 0) store(nxt);
+    // the MFMAs of tile kt between two scheduling fences: the loads before
+    // them, the LDS writes (which wait for loads) after them
+    auto fenced_compute = [&](int kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      compute(smem + (kt & 1) * STAGE);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // whole tile kt in stage S, tile kt + 1 in set S ^ 1: load tile kt + 2
+    // (clamped to the last whole tile, so the load count never varies) into
+    // set S, multiply, write set S ^ 1 to the other stage
+    auto whole_step = [&](int kt, auto S) {
+      constexpr int kO = S ^ 1;
+      load(min(kt + 2, KTw - 1) * BK, Whole{}, S);
+      fenced_compute(kt);
+      store(smem + kO * STAGE, std::integral_constant<int, kO>{});
       __syncthreads();
     };
     int kt = 0;
-    for (; kt + 1 < KTw; ++kt) iter(kt, std::integral_constant<int, 1>{});
-    for (; kt + 1 < KT; ++kt) iter(kt, std::integral_constant<int, 2>{});
-    if (kt < KT) iter(kt, std::integral_constant<int, 0>{});
+    for (; kt + 2 < KTw; kt += 2) {
+      whole_step(kt, S0{});
+      whole_step(kt + 1, S1{});
+    }
+    if (kt + 1 < KTw) {  // tile kt + 1 is whole and already in set 1
+      fenced_compute(kt);
+      store(smem + STAGE, S1{});
+      __syncthreads();
+      ++kt;
+    }
+    for (; kt + 1 < KT; ++kt) {  // the ragged rest, one tile ahead in set 0
+      load((kt + 1) * BK, Edge{}, S0{});
+      fenced_compute(kt);
+      store(smem + ((kt + 1) & 1) * STAGE, S0{});
+      __syncthreads();
+    }
+    if (kt < KT) compute(smem + (kt & 1) * STAGE);
   }
 
   // Epilogue: acc[i][j] holds the D^T piece for rows m0+wm0+32i.. and
