@@ -127,7 +127,7 @@ def sweep(steps, warmup):
         call = (M, N, K, dA, W.BF16, case.a_order, case.lda, dB, W.BF16, case.b_order,
                 case.ldb, dD, W.BF16, case.d_order, case.ldd)
         auto = tla.gemm_variant(*call)
-        for v in (1, 2):
+        for v in (0, 1, 2):
             def run():
                 tla.gemm_epilogue(*call, stream=stream.cuda_stream, variant=v)
             for _ in range(warmup):
@@ -146,6 +146,49 @@ def sweep(steps, warmup):
                 name, M, N, K, us, tf, 100 * tf / PEAK_BF16_TFLOPS, "←" if name == auto else ""))
             print(lines[-1], file=sys.stderr, flush=True)
         del dA, dB, dD
+    # pitches off 16-byte alignment (every leading dimension one element past
+    # its extent) and the ragged fp16 workload: the general kernel's cases
+    lines += ["", "| odd pitches | layout | M×N×K | µs | TFLOP/s | % peak | variant |",
+              "|---|---|---|---|---|---|---|"]
+    odd = []
+    for a_type, b_order in ((W.BF16, W.COL), (W.BF16, W.ROW), (W.E4M3, W.COL)):
+        c = W.GemmCase(name="sweep_odd", M=4096, N=4096, K=4096, a_type=a_type, b_type=a_type,
+                       d_type=W.BF16, b_order=b_order, seed=5)
+        c.lda += 1
+        c.ldb += 1
+        c.ldd += 1
+        odd.append(c)
+    odd.append(W.GEMM_F16_RAGGED)
+    for case in odd:
+        inp = W.gemm_inputs(case)
+        dA, dB = to_dev(inp["A"]), to_dev(inp["B"])
+        dC = to_dev(inp["C"]) if inp["C"] is not None else None
+        dD = torch.empty(case.M * case.ldd, dtype=torch.int16, device="cuda")
+        run = gemm_call(tla, case, dA, dB, dD, dC, None, stream)
+        for _ in range(warmup):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        tf = case.flops() / (us * 1e-6) / 1e12
+        peak = PEAK_FP8_TFLOPS if case.a_type == W.E4M3 else PEAK_BF16_TFLOPS
+        layout = "%s, A %s, B %s, lda %d, ldb %d%s" % (
+            {W.BF16: "bf16", W.F16: "fp16", W.E4M3: "e4m3"}[case.a_type],
+            "row" if case.a_order == W.ROW else "col", "row" if case.b_order == W.ROW else "col",
+            case.lda, case.ldb, ", C ldc %d, beta %g" % (case.ldc, case.beta) if case.has_c else "")
+        lines.append("| %s | %s | %d×%d×%d | %.1f | %.0f | %.1f | %s |" % (
+            case.name, layout, case.M, case.N, case.K, us, tf, 100 * tf / peak,
+            tla.gemm_variant(case.M, case.N, case.K, dA, case.a_type, case.a_order, case.lda, dB,
+                             case.b_type, case.b_order, case.ldb, dD, case.d_type, case.d_order,
+                             case.ldd, C=dC, c_type=case.c_type, ldc=case.ldc,
+                             alpha=case.alpha, beta=case.beta)))
+        print(lines[-1], file=sys.stderr, flush=True)
+        del dA, dB, dC, dD
     # convolution: every kernel that applies, forced through
     # tla_conv2d_fprop_variant with prepared arguments (a launch costs the
     # host a few microseconds, less than any of these kernels)

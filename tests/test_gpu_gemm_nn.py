@@ -7,8 +7,9 @@ the oracle:
   epilogue (alpha, beta*C, bias, ReLU), ragged M and N (N a multiple of 8,
   down to one 16-byte chunk), K from one k-tile up, and pitched operands
   with NaN padding;
-* the kernel choice: variant 1 at every size, variant 0 forcible (its own
-  transpose-read form), variant 3 refused, the general kernel forcible;
+* the kernel choice: variant 1 below 256 tiles of 256 x 256, variant 0
+  (its own transpose-read form) from there on, either forcible, variant 3
+  refused, the general kernel forcible;
 * the general kernel's own k-rows-of-n slab for pitches and bases off
   16-byte alignment: N and K ragged down to one element, misaligned bases;
 * random inputs at 2048 x 2048 x 1024 and 4096 x 4096 x 512 within the
@@ -118,9 +119,9 @@ def test_row_major_b_random_4096_two_group_kernel():
     case = W.GemmCase(name="nn_rand_big", M=4096, N=4096, K=512, a_type=W.BF16, b_type=W.BF16,
                       d_type=W.BF16, a_order=W.ROW, b_order=W.ROW, alpha=1.5, beta=0.5,
                       act=W.ACT_RELU, has_c=True, has_bias=True, seed=9)
-    assert G.variant(case) == "gemm_fast_128x128"
+    assert G.variant(case) == "gemm_pingpong_256x256"
     inp = W.gemm_inputs(case)
-    D = G.run_gemm(case, inp, sentinel=SENT, variant=0)
+    D = G.run_gemm(case, inp, sentinel=SENT)
     assert G.padding_untouched(case, D, SENT)
     got = og.decode(case.d_type, W.d_logical(case, D).copy())
     ok, worst = og.within_tolerance(got, G.oracle_ref(case, inp), case.tol)
