@@ -320,9 +320,9 @@ struct RegSlab {
 // n (2 BN bytes; 16-byte chunk c of row r stored at chunk c ^ 4 (r % 4)),
 // and load_frag_nt reads it back with ds_read_b64_tr_b16.  Consecutive
 // lanes walk the chunks of one k row, so a load instruction covers runs of
-// whole rows; tiles inside K and N move whole chunks through load16_split
-// (load_whole), edge tiles element by element with rows past K and columns
-// past N zero (load_edge).
+// whole rows; tiles inside K move whole chunks through load16_split
+// (load_whole), the ragged k-tile chunk by chunk with rows past K zero and
+// the chunk that crosses N element by element (load_edge).
 template <int BN, int BK>
 struct RegSlabNT {
   static constexpr int kRow = 2 * BN;
@@ -335,14 +335,19 @@ struct RegSlabNT {
   uint32_t hi[kI];
   uint32_t shifts;  // byte shift of chunk it in bits 4 it .. 4 it + 1
 
-  // k0 .. k0 + BK - 1 inside K and n0 .. n0 + BN - 1 inside N
+  // Rows k0 .. k0 + BK - 1 inside K, N >= 8.  A chunk that starts past N
+  // reads columns N - 8 .. N - 1 instead and the chunk that crosses N reads
+  // on past it: their columns past N only feed columns of D that are never
+  // stored.  Reading past N stays inside the matrix while a row follows
+  // (row k0 + BK - 1 below K - 1, or the tile inside N).
   __device__ __forceinline__ void load_whole(const uint8_t* __restrict__ base, int64_t ld, int n0,
-                                             int k0, int tid) {
+                                             int N, int k0, int tid) {
     shifts = 0;
 #pragma unroll
     for (int it = 0; it < kI; ++it) {
       const int sc = tid + kThreads * it, r = sc / kCh, c = sc % kCh;
-      const uint8_t* p = base + ((int64_t)(k0 + r) * ld + n0 + 8 * c) * 2;
+      const int gn = n0 + 8 * c;
+      const uint8_t* p = base + ((int64_t)(k0 + r) * ld + (gn < N ? gn : N - 8)) * 2;
       shifts |= load16_split(p, v[it], hi[it]) << (4 * it);
     }
   }
@@ -729,11 +734,13 @@ __device__ __forceinline__ void store16_even(uint8_t* p, const i32x4& v) {
 // (load16_split) and writes it into its region in the same swizzled layout,
 // and stores D row by row through store16_even.  Consecutive lanes cover a
 // row's consecutive chunks, so each access instruction spans whole rows
-// instead of 32 rows 8 bytes apart.
+// instead of 32 rows 8 bytes apart.  Only the first `rows` rows of the wave
+// tile are in D: C reads of the others repeat the last one, and they store
+// nothing.
 template <int kAct, bool kDBf16, bool kHasC, int FM, int FN>
 __device__ __forceinline__ void epilogue_lds_any(const GemmParams& p, int m_base, int n_base,
                                                  int lane, const f32x16 (&acc)[FM][FN],
-                                                 uint8_t* region) {
+                                                 uint8_t* region, int rows) {
   constexpr int kRowB = 64 * FN, kCh = kRowB / 16, kRowsPerKiB = 1024 / kRowB;
   static_assert(kCh == 4 || kCh == 8 || kCh == 16, "row width");
   constexpr int kIters = 32 * FM * kRowB / 1024;
@@ -747,7 +754,8 @@ __device__ __forceinline__ void epilogue_lds_any(const GemmParams& p, int m_base
     uint32_t hi[kIters], shifts = 0;
     static_for<kIters>([&](auto t) {
       const int r = kRowsPerKiB * t + rr;
-      shifts |= load16_split(C + (int64_t)r * p.c_sm * 2 + swz(r, cs) * 16, lo[t], hi[t]) << (4 * t);
+      const int rc = min(r, rows - 1);
+      shifts |= load16_split(C + (int64_t)rc * p.c_sm * 2 + swz(r, cs) * 16, lo[t], hi[t]) << (4 * t);
     });
     static_for<kIters>([&](auto t) {
       *(i32x4*)(region + t * 1024 + lane * 16) = realign16(lo[t], hi[t], shifts >> (4 * t));
@@ -771,7 +779,7 @@ __device__ __forceinline__ void epilogue_lds_any(const GemmParams& p, int m_base
   static_for<kIters>([&](auto t) {
     const int r = kRowsPerKiB * t + rr;
     const i32x4 v = *(const i32x4*)(region + t * 1024 + lane * 16);
-    store16_even(D + (int64_t)r * p.d_sm * 2 + swz(r, cs) * 16, v);
+    if (r < rows) store16_even(D + (int64_t)r * p.d_sm * 2 + swz(r, cs) * 16, v);
   });
 }
 
@@ -814,36 +822,42 @@ __device__ __forceinline__ void epilogue_direct(const GemmParams& p, int m_base,
 // even address
 template <int kForm, int kAct, bool kDBf16, int FM, int FN>
 __device__ __forceinline__ void epilogue_fast(const GemmParams& p, int m_base, int n_base, int lane,
-                                              const f32x16 (&acc)[FM][FN], uint8_t* region) {
+                                              const f32x16 (&acc)[FM][FN], uint8_t* region,
+                                              int rows) {
   const bool has_c = p.beta != 0.f;
   if constexpr (kForm == 1) {
     if (has_c) epilogue_lds<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc, region);
     else epilogue_lds<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc, region);
   } else if constexpr (kForm == 2) {
-    if (has_c) epilogue_lds_any<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc, region);
-    else epilogue_lds_any<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc, region);
+    if (has_c)
+      epilogue_lds_any<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc, region, rows);
+    else
+      epilogue_lds_any<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc, region, rows);
   } else {
     if (has_c) epilogue_direct<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc);
     else epilogue_direct<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc);
   }
 }
 
+// rows: the wave tile's rows inside D (kForm 2 only; the others take whole
+// tiles)
 template <int kForm, int FM, int FN>
 __device__ __forceinline__ void epilogue_switch(const GemmParams& p, int m_base, int n_base, int lane,
-                                                const f32x16 (&acc)[FM][FN], uint8_t* region) {
+                                                const f32x16 (&acc)[FM][FN], uint8_t* region,
+                                                int rows = 32 * FM) {
   const bool dbf = p.d_type == kBF16;
   switch (p.act) {
     case TLA_ACT_RELU:
-      if (dbf) epilogue_fast<kForm, TLA_ACT_RELU, true>(p, m_base, n_base, lane, acc, region);
-      else epilogue_fast<kForm, TLA_ACT_RELU, false>(p, m_base, n_base, lane, acc, region);
+      if (dbf) epilogue_fast<kForm, TLA_ACT_RELU, true>(p, m_base, n_base, lane, acc, region, rows);
+      else epilogue_fast<kForm, TLA_ACT_RELU, false>(p, m_base, n_base, lane, acc, region, rows);
       break;
     case TLA_ACT_GELU:
-      if (dbf) epilogue_fast<kForm, TLA_ACT_GELU, true>(p, m_base, n_base, lane, acc, region);
-      else epilogue_fast<kForm, TLA_ACT_GELU, false>(p, m_base, n_base, lane, acc, region);
+      if (dbf) epilogue_fast<kForm, TLA_ACT_GELU, true>(p, m_base, n_base, lane, acc, region, rows);
+      else epilogue_fast<kForm, TLA_ACT_GELU, false>(p, m_base, n_base, lane, acc, region, rows);
       break;
     default:
-      if (dbf) epilogue_fast<kForm, TLA_ACT_NONE, true>(p, m_base, n_base, lane, acc, region);
-      else epilogue_fast<kForm, TLA_ACT_NONE, false>(p, m_base, n_base, lane, acc, region);
+      if (dbf) epilogue_fast<kForm, TLA_ACT_NONE, true>(p, m_base, n_base, lane, acc, region, rows);
+      else epilogue_fast<kForm, TLA_ACT_NONE, false>(p, m_base, n_base, lane, acc, region, rows);
       break;
   }
 }
@@ -855,9 +869,11 @@ __device__ __forceinline__ void epilogue_switch(const GemmParams& p, int m_base,
 // null.  A wave tile inside D whose C (if any) and bias (if any) have D's
 // 16-bit type takes the LDS path when C and D rows allow 16-byte vectors,
 // else the direct path with 8-byte vectors, else (kAny, row-major C and D
-// at even addresses, any pitch) the LDS path with realigned row accesses;
-// anything else (edge tiles, fp32 or mixed-type C or bias, column-major C
-// or D) goes group by group through the predicated epilogue4.
+// at even addresses, any pitch) the LDS path with realigned row accesses,
+// which (kAny) also takes wave tiles that end inside M but not inside N;
+// anything else (other edge tiles, fp32 or mixed-type C or bias,
+// column-major C or D) goes group by group through the predicated
+// epilogue4.
 template <int FM, int FN, bool kAny = false>
 __device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, int n_base, int lane,
                                                const f32x16 (&acc)[FM][FN], uint8_t* region) {
@@ -868,9 +884,10 @@ __device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, 
     epilogue_switch<1, FM, FN>(p, m_base, n_base, lane, acc, region);
   } else if (full && b_ok && (p.flags & kDVec) && (p.beta == 0.f || (c16 && (p.flags & kCVec)))) {
     epilogue_switch<0, FM, FN>(p, m_base, n_base, lane, acc, region);
-  } else if (kAny && full && b_ok && region && (p.flags & kD2) &&
-             (p.beta == 0.f || (c16 && (p.flags & kC2)))) {
-    if constexpr (kAny) epilogue_switch<2, FM, FN>(p, m_base, n_base, lane, acc, region);
+  } else if (kAny && m_base < p.M && n_base + 32 * FN <= p.N && b_ok && region &&
+             (p.flags & kD2) && (p.beta == 0.f || (c16 && (p.flags & kC2)))) {
+    if constexpr (kAny)
+      epilogue_switch<2, FM, FN>(p, m_base, n_base, lane, acc, region, min(32 * FM, p.M - m_base));
   } else {
     static_for<FM>([&](auto i) {
       const int m = m_base + 32 * i + mfma32_acc_col(lane, 0);

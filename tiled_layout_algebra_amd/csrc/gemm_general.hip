@@ -164,9 +164,8 @@ __global__ __launch_bounds__(kThreads, (kFast || !kAKC || kBView == kBN) ? 1 : 2
       });
     };
     static_assert(!kConv || !kFast, "the convolution view uses the register-staged path");
-    // Two register sets per operand.  Tiles 0 .. KTw - 1 lie inside K (and,
-    // for the k-rows-of-n B slab, inside N); they load as whole chunks with
-    // no per-lane branch, two tiles ahead: tile t + 2 goes into set t % 2
+    // Two register sets per operand.  Tiles 0 .. KTw - 1 lie inside K; they
+    // load as whole chunks with no per-lane branch, two tiles ahead: tile t + 2 goes into set t % 2
     // before the MFMAs of tile t, and set (t + 1) % 2 (tile t + 1, loaded a
     // whole iteration earlier) is written to the other LDS stage after them.
     // The ragged rest goes one tile ahead through the element-wise loader.
@@ -186,7 +185,7 @@ __global__ __launch_bounds__(kThreads, (kFast || !kAKC || kBView == kBN) ? 1 : 2
         else ra[set].load_edge(p.A, a_s, m0, p.M, k0, p.K, tid);
       }
       if constexpr (kNT) {
-        if constexpr (whole) rb[set].load_whole(p.B, b_s, n0, k0, tid);
+        if constexpr (whole) rb[set].load_whole(p.B, b_s, n0, p.N, k0, tid);
         else rb[set].load_edge(p.B, b_s, n0, p.N, k0, p.K, tid);
       } else {
         if constexpr (whole && kBView == kBK) rb[set].load_whole(p.B, b_s, n0, p.N, k0, tid);
@@ -201,7 +200,9 @@ __global__ __launch_bounds__(kThreads, (kFast || !kAKC || kBView == kBN) ? 1 : 2
     using S1 = std::integral_constant<int, 1>;
     using Whole = std::true_type;
     using Edge = std::false_type;
-    const int KTw = (kNT && n0 + BN > p.N) ? 0 : p.K / BK;
+    // whole tiles: inside K; for the k-rows-of-n slab of a tile that crosses
+    // N also before the tile holding row K - 1 (its chunks read past N)
+    const int KTw = (kNT && n0 + BN > p.N) ? (p.N >= 8 ? (p.K - 1) / BK : 0) : p.K / BK;
     if (KT > 0) {
       if (KTw > 0) load(0, Whole{}, S0{});
       else load(0, Edge{}, S0{});
