@@ -258,6 +258,28 @@ def test_realigned_loads_bit_exact(a_order, b_order, a_type, pad):
     assert np.array_equal(W.d_logical(case, D), want)
 
 
+@pytest.mark.parametrize("b_order", [W.ROW, W.COL])
+@pytest.mark.parametrize("a_type", [W.F16, W.BF16])
+@pytest.mark.parametrize("M,N,K", [(300, 264, 200), (7, 40, 131), (1031, 257, 777)])
+def test_column_major_a_bit_exact(M, N, K, a_type, b_order):
+    """A column-major (M-contiguous) with a pitch past M: the general
+    kernel holds it as k rows of m, the tiles that cross M reading on past
+    it into NaN-filled pitch padding (rows of D past M are never stored);
+    integer inputs, so D is exact."""
+    case = W.GemmCase(name="acol", M=M, N=N, K=K, a_type=a_type, b_type=a_type, d_type=a_type,
+                      a_order=W.COL, b_order=b_order, alpha=1.5, beta=0.5, act=W.ACT_RELU,
+                      has_c=True, has_bias=True, seed=M + N + K, dist_a="int3", dist_b="int3",
+                      dist_c="int3", dist_bias="eighths")
+    case.lda += 5
+    case.ldb += 3
+    assert G.variant(case) == "gemm_general_128x128"
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT[a_type])
+    assert G.padding_untouched(case, D, SENT[a_type])
+    want = W.encode(G.oracle_ref(case, inp), a_type).reshape(M, N)
+    assert np.array_equal(W.d_logical(case, D), want)
+
+
 def test_c_aliases_d():
     case = _small(M=200, N=136, K=64)
     inp = W.gemm_inputs(case)

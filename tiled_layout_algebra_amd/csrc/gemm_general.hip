@@ -27,20 +27,23 @@ namespace {
 //
 // Register-staged operand views (fixed per instantiation, so the loader
 // carries no stride it does not use): kAKC, A is K-contiguous (row-major),
-// else M-contiguous; kBView: B K-contiguous (kBK), N-contiguous through
-// element loads (kBN), or N-contiguous 16-bit with its slab as k rows of n
-// (RegSlabNT) read into fragments by transposing LDS reads (kBNT).
+// else M-contiguous -- 16-bit A then has its slab as k rows of m
+// (RegSlabNT), e4m3 A goes through element loads; kBView: B K-contiguous
+// (kBK), N-contiguous through element loads (kBN), or N-contiguous 16-bit
+// with its slab as k rows of n (RegSlabNT, kBNT).  A k-rows slab is read
+// into fragments by transposing LDS reads.
 enum : int { kBK = 0, kBN = 1, kBNT = 2 };
 
-// The register-staged form with K-contiguous or k-rows-of-n operands asks
-// for two waves per SIMD (at most 256 VGPRs): left to itself the compiler
-// let its two register sets push the kernel to 260-316 VGPRs, one wave per
-// SIMD.  With an element-wise view it would spill, so those keep one.
+// The register-staged form without element-wise views asks for two waves
+// per SIMD (at most 256 VGPRs): left to itself the compiler let its two
+// register sets push the kernel to 260-316 VGPRs, one wave per SIMD.  With
+// an element-wise view it would spill, so those keep one.
 template <int kCode, int BM, int BN, int kRowBytes, int kStages, bool kFast, bool kConv = false,
           bool kAKC = true, int kBView = kBK>
-__global__ __launch_bounds__(kThreads, (kFast || !kAKC || kBView == kBN) ? 1 : 2) void gemm_kernel(
-    const GemmParams p) {
+__global__ __launch_bounds__(kThreads, (kFast || (!kAKC && elem_bytes(kCode) != 2) ||
+                                        kBView == kBN) ? 1 : 2) void gemm_kernel(const GemmParams p) {
   constexpr bool kNT = kBView == kBNT;
+  constexpr bool kAT = !kAKC && elem_bytes(kCode) == 2;  // A as k rows of m
   using Atom = MfmaAtom<kCode>;
   using Frag = typename Atom::Frag;
   constexpr int EB = elem_bytes(kCode);
@@ -71,7 +74,10 @@ __global__ __launch_bounds__(kThreads, (kFast || !kAKC || kBView == kBN) ? 1 : 2
   Frag a[2][FM], b[2][FN];
   auto read_frags = [&](auto buf, const uint8_t* stage, auto ks) {
     static_for<FM>([&](auto i) {
-      a[buf][i] = load_frag<kCode, kRowBytes>(stage, wm0 + 32 * i + (lane & 31), ks, lane);
+      if constexpr (kAT)
+        a[buf][i] = load_frag_nt<2 * BM>(stage, wm0 + 32 * i, ks, lane);
+      else
+        a[buf][i] = load_frag<kCode, kRowBytes>(stage, wm0 + 32 * i + (lane & 31), ks, lane);
     });
     static_for<FN>([&](auto j) {
       if constexpr (kNT)
@@ -170,7 +176,9 @@ __global__ __launch_bounds__(kThreads, (kFast || !kAKC || kBView == kBN) ? 1 : 2
     // whole iteration earlier) is written to the other LDS stage after them.
     // The ragged rest goes one tile ahead through the element-wise loader.
     // Tile t lives in LDS stage t % 2.
-    using RA = std::conditional_t<kConv, ConvSlab<BM, EB, kRowBytes>, RegSlab<BM, EB, kRowBytes, kAKC>>;
+    using RA = std::conditional_t<
+        kConv, ConvSlab<BM, EB, kRowBytes>,
+        std::conditional_t<kAT, RegSlabNT<BM, BK>, RegSlab<BM, EB, kRowBytes, kAKC>>>;
     using RB = std::conditional_t<kNT, RegSlabNT<BN, BK>, RegSlab<BN, EB, kRowBytes, kBView == kBK>>;
     RA ra[2];
     RB rb[2];
@@ -181,8 +189,13 @@ __global__ __launch_bounds__(kThreads, (kFast || !kAKC || kBView == kBN) ? 1 : 2
       if constexpr (kConv) {
         ra[set].load_conv(p, m0, k0, a_vec, tid);
       } else {
-        if constexpr (whole && kAKC) ra[set].load_whole(p.A, a_s, m0, p.M, k0, tid);
-        else ra[set].load_edge(p.A, a_s, m0, p.M, k0, p.K, tid);
+        if constexpr (kAT) {
+          if constexpr (whole) ra[set].load_whole(p.A, a_s, m0, p.M, k0, tid);
+          else ra[set].load_edge(p.A, a_s, m0, p.M, k0, p.K, tid);
+        } else {
+          if constexpr (whole && kAKC) ra[set].load_whole(p.A, a_s, m0, p.M, k0, tid);
+          else ra[set].load_edge(p.A, a_s, m0, p.M, k0, p.K, tid);
+        }
       }
       if constexpr (kNT) {
         if constexpr (whole) rb[set].load_whole(p.B, b_s, n0, p.N, k0, tid);
@@ -200,9 +213,12 @@ __global__ __launch_bounds__(kThreads, (kFast || !kAKC || kBView == kBN) ? 1 : 2
     using S1 = std::integral_constant<int, 1>;
     using Whole = std::true_type;
     using Edge = std::false_type;
-    // whole tiles: inside K; for the k-rows-of-n slab of a tile that crosses
-    // N also before the tile holding row K - 1 (its chunks read past N)
-    const int KTw = (kNT && n0 + BN > p.N) ? (p.N >= 8 ? (p.K - 1) / BK : 0) : p.K / BK;
+    // whole tiles: inside K; for a k-rows slab of a tile that crosses M or N
+    // also before the tile holding row K - 1 (its chunks read past the edge)
+    const bool m_edge = kAT && m0 + BM > p.M, n_edge = kNT && n0 + BN > p.N;
+    const int KTw = (m_edge || n_edge)
+                        ? ((m_edge && p.M < 8) || (n_edge && p.N < 8) ? 0 : (p.K - 1) / BK)
+                        : p.K / BK;
     if (KT > 0) {
       if (KTw > 0) load(0, Whole{}, S0{});
       else load(0, Edge{}, S0{});
