@@ -280,6 +280,30 @@ def test_column_major_a_bit_exact(M, N, K, a_type, b_order):
     assert np.array_equal(W.d_logical(case, D), want)
 
 
+@pytest.mark.parametrize("b_order", [W.ROW, W.COL])
+@pytest.mark.parametrize("a_type", [W.F16, W.BF16])
+@pytest.mark.parametrize("M,N,K", [(130, 201, 96), (70, 4223, 64), (257, 69, 40), (65, 4129, 16)])
+def test_odd_pitch_epilogue_edges_bit_exact(M, N, K, a_type, b_order):
+    """C and D at odd pitches with a bias: wave tiles that end inside M, or
+    inside N with at least half their columns in D, take the any-pitch LDS
+    epilogue (row-predicated stores, the chunk that crosses N element by
+    element, bias groups past N clamped), narrower ones the per-group path;
+    integer inputs, so D is exact and D's padding keeps its sentinel."""
+    case = W.GemmCase(name="epi_edges", M=M, N=N, K=K, a_type=a_type, b_type=a_type,
+                      d_type=a_type, b_order=b_order, alpha=1.5, beta=0.5, act=W.ACT_RELU,
+                      has_c=True, has_bias=True, seed=M + 2 * N + K, dist_a="int3",
+                      dist_b="int3", dist_c="int3", dist_bias="eighths")
+    case.lda += 1
+    case.ldc += 3
+    case.ldd += 5
+    assert G.variant(case) == "gemm_general_128x128"
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT[a_type])
+    assert G.padding_untouched(case, D, SENT[a_type])
+    want = W.encode(G.oracle_ref(case, inp), a_type).reshape(M, N)
+    assert np.array_equal(W.d_logical(case, D), want)
+
+
 def test_c_aliases_d():
     case = _small(M=200, N=136, K=64)
     inp = W.gemm_inputs(case)

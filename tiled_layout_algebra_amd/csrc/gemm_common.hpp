@@ -652,13 +652,22 @@ __device__ __forceinline__ uint2 epi_group(const f32x16& acc, int g, uint2 c, ui
 
 // This lane's 16-bit bias values for its column groups, all loads issued
 // before any is used (zero bits when there is no bias).
+// cols: the wave tile's columns inside D; a group past them reads the
+// aligned group that holds the last column instead (bias is 8-byte aligned,
+// so that read stays on the last element's page), feeding only columns of D
+// that are never stored.
 template <int FN>
 __device__ __forceinline__ void load_bias16(const GemmParams& p, int n_base, int half,
-                                            uint2 (&braw)[FN][4]) {
+                                            uint2 (&braw)[FN][4], int cols = 32 * FN) {
   static_for<FN>([&](auto j) { static_for<4>([&](auto g) { braw[j][g] = uint2{0u, 0u}; }); });
   if (p.bias) {
-    const uint2* b = (const uint2*)((const uint16_t*)p.bias + n_base + 4 * half);
-    static_for<FN>([&](auto j) { static_for<4>([&](auto g) { braw[j][g] = b[8 * j + 2 * g]; }); });
+    const uint16_t* b = (const uint16_t*)p.bias + n_base;
+    const int last4 = (cols - 1) & ~3;
+    static_for<FN>([&](auto j) {
+      static_for<4>([&](auto g) {
+        braw[j][g] = *(const uint2*)(b + min(32 * j + 8 * g + 4 * half, last4));
+      });
+    });
   }
 }
 
@@ -734,13 +743,14 @@ __device__ __forceinline__ void store16_even(uint8_t* p, const i32x4& v) {
 // (load16_split) and writes it into its region in the same swizzled layout,
 // and stores D row by row through store16_even.  Consecutive lanes cover a
 // row's consecutive chunks, so each access instruction spans whole rows
-// instead of 32 rows 8 bytes apart.  Only the first `rows` rows of the wave
-// tile are in D: C reads of the others repeat the last one, and they store
-// nothing.
+// instead of 32 rows 8 bytes apart.  Only the first `rows` rows and `cols`
+// columns of the wave tile are in D: C reads of the other rows repeat the
+// last one and they store nothing; in a tile that ends inside N the chunk
+// that crosses N moves element by element and chunks past it are skipped.
 template <int kAct, bool kDBf16, bool kHasC, int FM, int FN>
 __device__ __forceinline__ void epilogue_lds_any(const GemmParams& p, int m_base, int n_base,
                                                  int lane, const f32x16 (&acc)[FM][FN],
-                                                 uint8_t* region, int rows) {
+                                                 uint8_t* region, int rows, int cols) {
   constexpr int kRowB = 64 * FN, kCh = kRowB / 16, kRowsPerKiB = 1024 / kRowB;
   static_assert(kCh == 4 || kCh == 8 || kCh == 16, "row width");
   constexpr int kIters = 32 * FM * kRowB / 1024;
@@ -748,22 +758,42 @@ __device__ __forceinline__ void epilogue_lds_any(const GemmParams& p, int m_base
   auto swz = [](int r, int c) { return c ^ ((r / (16 / kCh)) & (kCh - 1)); };
   const int row = lane & 31, half = lane >> 5;
   const int rr = lane / kCh, cs = lane % kCh;  // row-wise view of one KiB
+  const bool all_cols = cols == 32 * FN;
   if constexpr (kHasC) {
     const uint8_t* C = p.C + ((int64_t)m_base * p.c_sm + n_base) * 2;
-    i32x4 lo[kIters];
-    uint32_t hi[kIters], shifts = 0;
-    static_for<kIters>([&](auto t) {
-      const int r = kRowsPerKiB * t + rr;
-      const int rc = min(r, rows - 1);
-      shifts |= load16_split(C + (int64_t)rc * p.c_sm * 2 + swz(r, cs) * 16, lo[t], hi[t]) << (4 * t);
-    });
-    static_for<kIters>([&](auto t) {
-      *(i32x4*)(region + t * 1024 + lane * 16) = realign16(lo[t], hi[t], shifts >> (4 * t));
-    });
+    if (all_cols) {
+      i32x4 lo[kIters];
+      uint32_t hi[kIters], shifts = 0;
+      static_for<kIters>([&](auto t) {
+        const int r = kRowsPerKiB * t + rr;
+        const int rc = min(r, rows - 1);
+        shifts |= load16_split(C + (int64_t)rc * p.c_sm * 2 + swz(r, cs) * 16, lo[t], hi[t])
+                  << (4 * t);
+      });
+      static_for<kIters>([&](auto t) {
+        *(i32x4*)(region + t * 1024 + lane * 16) = realign16(lo[t], hi[t], shifts >> (4 * t));
+      });
+    } else {
+      static_for<kIters>([&](auto t) {
+        const int r = kRowsPerKiB * t + rr;
+        const int c0 = 8 * swz(r, cs);  // first column of the chunk
+        const uint8_t* rowp = C + (int64_t)min(r, rows - 1) * p.c_sm * 2;
+        i32x4 x = {0, 0, 0, 0};
+        if (c0 + 8 <= cols) {
+          i32x4 lo;
+          uint32_t hi;
+          const uint32_t sh = load16_split(rowp + c0 * 2, lo, hi);
+          x = realign16(lo, hi, sh);
+        } else if (c0 < cols) {
+          x = gather16<2>(rowp, 2, c0, cols, cols - 1);
+        }
+        *(i32x4*)(region + t * 1024 + lane * 16) = x;
+      });
+    }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
   uint2 braw[FN][4];
-  load_bias16<FN>(p, n_base, half, braw);
+  load_bias16<FN>(p, n_base, half, braw, cols);
   static_for<FM>([&](auto i) {
     static_for<FN>([&](auto j) {
       static_for<4>([&](auto g) {
@@ -778,8 +808,18 @@ __device__ __forceinline__ void epilogue_lds_any(const GemmParams& p, int m_base
   uint8_t* D = p.D + ((int64_t)m_base * p.d_sm + n_base) * 2;
   static_for<kIters>([&](auto t) {
     const int r = kRowsPerKiB * t + rr;
+    const int c0 = 8 * swz(r, cs);
     const i32x4 v = *(const i32x4*)(region + t * 1024 + lane * 16);
-    if (r < rows) store16_even(D + (int64_t)r * p.d_sm * 2 + swz(r, cs) * 16, v);
+    uint8_t* dst = D + (int64_t)r * p.d_sm * 2 + c0 * 2;
+    if (r < rows) {
+      if (c0 + 8 <= cols) {
+        store16_even(dst, v);
+      } else if (c0 < cols) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c0 + e < cols) ((uint16_t*)dst)[e] = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
+      }
+    }
   });
 }
 
@@ -823,42 +863,40 @@ __device__ __forceinline__ void epilogue_direct(const GemmParams& p, int m_base,
 template <int kForm, int kAct, bool kDBf16, int FM, int FN>
 __device__ __forceinline__ void epilogue_fast(const GemmParams& p, int m_base, int n_base, int lane,
                                               const f32x16 (&acc)[FM][FN], uint8_t* region,
-                                              int rows) {
+                                              int rows, int cols) {
   const bool has_c = p.beta != 0.f;
   if constexpr (kForm == 1) {
     if (has_c) epilogue_lds<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc, region);
     else epilogue_lds<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc, region);
   } else if constexpr (kForm == 2) {
     if (has_c)
-      epilogue_lds_any<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc, region, rows);
+      epilogue_lds_any<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc, region, rows,
+                                                   cols);
     else
-      epilogue_lds_any<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc, region, rows);
+      epilogue_lds_any<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc, region, rows,
+                                                    cols);
   } else {
     if (has_c) epilogue_direct<kAct, kDBf16, true, FM, FN>(p, m_base, n_base, lane, acc);
     else epilogue_direct<kAct, kDBf16, false, FM, FN>(p, m_base, n_base, lane, acc);
   }
 }
 
-// rows: the wave tile's rows inside D (kForm 2 only; the others take whole
-// tiles)
+// rows, cols: the wave tile's rows and columns inside D (kForm 2 only; the
+// others take whole tiles)
 template <int kForm, int FM, int FN>
 __device__ __forceinline__ void epilogue_switch(const GemmParams& p, int m_base, int n_base, int lane,
                                                 const f32x16 (&acc)[FM][FN], uint8_t* region,
-                                                int rows = 32 * FM) {
+                                                int rows = 32 * FM, int cols = 32 * FN) {
   const bool dbf = p.d_type == kBF16;
+  auto run = [&](auto act) {
+    constexpr int kAct = decltype(act)::value;
+    if (dbf) epilogue_fast<kForm, kAct, true>(p, m_base, n_base, lane, acc, region, rows, cols);
+    else epilogue_fast<kForm, kAct, false>(p, m_base, n_base, lane, acc, region, rows, cols);
+  };
   switch (p.act) {
-    case TLA_ACT_RELU:
-      if (dbf) epilogue_fast<kForm, TLA_ACT_RELU, true>(p, m_base, n_base, lane, acc, region, rows);
-      else epilogue_fast<kForm, TLA_ACT_RELU, false>(p, m_base, n_base, lane, acc, region, rows);
-      break;
-    case TLA_ACT_GELU:
-      if (dbf) epilogue_fast<kForm, TLA_ACT_GELU, true>(p, m_base, n_base, lane, acc, region, rows);
-      else epilogue_fast<kForm, TLA_ACT_GELU, false>(p, m_base, n_base, lane, acc, region, rows);
-      break;
-    default:
-      if (dbf) epilogue_fast<kForm, TLA_ACT_NONE, true>(p, m_base, n_base, lane, acc, region, rows);
-      else epilogue_fast<kForm, TLA_ACT_NONE, false>(p, m_base, n_base, lane, acc, region, rows);
-      break;
+    case TLA_ACT_RELU: run(std::integral_constant<int, TLA_ACT_RELU>{}); break;
+    case TLA_ACT_GELU: run(std::integral_constant<int, TLA_ACT_GELU>{}); break;
+    default: run(std::integral_constant<int, TLA_ACT_NONE>{}); break;
   }
 }
 
@@ -870,10 +908,11 @@ __device__ __forceinline__ void epilogue_switch(const GemmParams& p, int m_base,
 // 16-bit type takes the LDS path when C and D rows allow 16-byte vectors,
 // else the direct path with 8-byte vectors, else (kAny, row-major C and D
 // at even addresses, any pitch) the LDS path with realigned row accesses,
-// which (kAny) also takes wave tiles that end inside M but not inside N;
-// anything else (other edge tiles, fp32 or mixed-type C or bias,
-// column-major C or D) goes group by group through the predicated
-// epilogue4.
+// which (kAny) also takes wave tiles that end inside M, or inside N with
+// at least half their columns in D (narrower ones spend less in epilogue4,
+// whose groups past N return at once); anything else (other edge tiles,
+// fp32 or mixed-type C or bias, column-major C or D) goes group by group
+// through the predicated epilogue4.
 template <int FM, int FN, bool kAny = false>
 __device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, int n_base, int lane,
                                                const f32x16 (&acc)[FM][FN], uint8_t* region) {
@@ -884,10 +923,11 @@ __device__ __forceinline__ void epilogue_tiles(const GemmParams& p, int m_base, 
     epilogue_switch<1, FM, FN>(p, m_base, n_base, lane, acc, region);
   } else if (full && b_ok && (p.flags & kDVec) && (p.beta == 0.f || (c16 && (p.flags & kCVec)))) {
     epilogue_switch<0, FM, FN>(p, m_base, n_base, lane, acc, region);
-  } else if (kAny && m_base < p.M && n_base + 32 * FN <= p.N && b_ok && region &&
+  } else if (kAny && m_base < p.M && p.N - n_base >= 16 * FN && b_ok && region &&
              (p.flags & kD2) && (p.beta == 0.f || (c16 && (p.flags & kC2)))) {
     if constexpr (kAny)
-      epilogue_switch<2, FM, FN>(p, m_base, n_base, lane, acc, region, min(32 * FM, p.M - m_base));
+      epilogue_switch<2, FM, FN>(p, m_base, n_base, lane, acc, region, min(32 * FM, p.M - m_base),
+                                 min(32 * FN, p.N - n_base));
   } else {
     static_for<FM>([&](auto i) {
       const int m = m_base + 32 * i + mfma32_acc_col(lane, 0);
