@@ -139,15 +139,17 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  *   3 "gemm_fast_256x256"    256x256 tiles, one group (16-bit: 8 wavefronts
  *                            of 128x64; e4m3: 4 of 128x128), direct copies
  * tla_gemm_epilogue picks one from the problem: in the fast layout,
- * variant 0 with at least 128 tiles of 256x256 and 1 otherwise; variant 1
- * in the N-contiguous-B layout; variant 2 outside both;
+ * variant 0 with at least 128 tiles of 256x256 and 1 otherwise; in the
+ * N-contiguous-B layout, variant 0 with at least 256 tiles of 256x256 and 1
+ * otherwise; variant 2 outside both;
  * tla_gemm_run_variant runs the one asked for, with the same semantics and
  * tolerance, or returns TLA_ERR_UNSUPPORTED when a fast variant is asked
  * for a problem without the fast layout (both operands K-contiguous,
- * 16-byte aligned rows, K a multiple of 128 bytes, each operand < 2 GiB) --
- * variants 0 and 1 also accept the N-contiguous-B layout (16-bit operands;
- * A as in the fast layout; B row-major with 16-byte aligned rows, N a
- * multiple of 8, K a multiple of 64, B below 2 GiB).
+ * 16-byte aligned rows, K a multiple of 8 for 16-bit operands -- the last
+ * k-tile may end inside the 64-element slab -- or of 128 for e4m3, each
+ * operand < 2 GiB) -- variants 0 and 1 also accept the N-contiguous-B layout
+ * (16-bit operands; A as in the fast layout; B row-major with 16-byte
+ * aligned rows, N and K multiples of 8, B below 2 GiB).
  * Variant ids outside [0, TLA_GEMM_VARIANTS) are TLA_ERR_INVALID_ARG.
  */
 #define TLA_GEMM_VARIANTS 4

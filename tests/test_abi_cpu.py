@@ -108,12 +108,18 @@ def test_gemm_variant_choice():
     assert _variant(_args(**dict(big_nn, M=3072, N=3072, ldb=3072, ldd=3072)))[1] == "gemm_fast_128x128"
     assert _variant(_args(**dict(big_nn, M=4096 - 256)))[1] == "gemm_fast_128x128"  # 240 tiles
     assert _variant(_args(**dict(big_nn, M=4096 - 255)))[1] == "gemm_pingpong_256x256"  # 256
-    # ... but not for e4m3, N not a multiple of 8, unaligned B rows or ragged K
+    # ... but not for e4m3, N not a multiple of 8, unaligned B rows or K off
+    # the 16-byte chunk
     assert _variant(_args(**dict(e4, b_order=tla.ROW_MAJOR)))[1] == "gemm_general_128x128"
     assert _variant(_args(b_order=tla.ROW_MAJOR, N=60, ldd=60, ldb=60))[1] == "gemm_general_128x128"
     assert _variant(_args(b_order=tla.ROW_MAJOR, ldb=67))[1] == "gemm_general_128x128"
-    assert _variant(_args(b_order=tla.ROW_MAJOR, K=96, lda=96))[1] == "gemm_general_128x128"
-    # odd pitches, misaligned bases, ragged K: general
+    assert _variant(_args(b_order=tla.ROW_MAJOR, K=92, lda=96))[1] == "gemm_general_128x128"
+    # 16-bit K a multiple of 8 but not of the 64-element slab: still fast
+    assert _variant(_args(b_order=tla.ROW_MAJOR, K=96, lda=96))[1] == "gemm_fast_128x128"
+    assert _variant(_args(K=96, lda=96, ldb=96))[1] == "gemm_fast_128x128"
+    big_k = dict(M=4096, N=4096, K=4000, lda=4096, ldb=4096, ldd=4096)
+    assert _variant(_args(**big_k))[1] == "gemm_pingpong_256x256"
+    # odd pitches, misaligned bases, K off the chunk: general
     assert _variant(_args(lda=65))[1] == "gemm_general_128x128"
     assert _variant(_args(A=FAKE + 2))[1] == "gemm_general_128x128"
     assert _variant(_args(K=63, lda=64, ldb=64))[1] == "gemm_general_128x128"

@@ -304,6 +304,59 @@ def test_odd_pitch_epilogue_edges_bit_exact(M, N, K, a_type, b_order):
     assert np.array_equal(W.d_logical(case, D), want)
 
 
+@pytest.mark.parametrize("variant", [0, 1, 3])
+@pytest.mark.parametrize("a_type", [W.F16, W.BF16])
+@pytest.mark.parametrize("K,pad", [(8, 0), (72, 8), (200, 0), (1000, 24)])
+def test_fast_kernels_ragged_k_bit_exact(K, pad, a_type, variant):
+    """16-bit K a multiple of 8 but not of the 64-element slab, on the
+    direct-copy kernels: the last k-tile's chunks past K read zeros through
+    the buffer range check.  With pad > 0 those chunks are the NaN-filled
+    pitch padding, with pad = 0 the next row's data; either would show in D."""
+    M, N = 300, 520
+    case = W.GemmCase(name="ragged_k", M=M, N=N, K=K, a_type=a_type, b_type=a_type,
+                      d_type=a_type, alpha=1.5, beta=0.5, act=W.ACT_RELU, has_c=True,
+                      has_bias=True, seed=K + variant, dist_a="int3", dist_b="int3",
+                      dist_c="int3", dist_bias="eighths")
+    case.lda += pad
+    case.ldb += pad
+    assert G.variant(case) in ("gemm_fast_128x128", "gemm_pingpong_256x256")
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT[a_type], variant=variant)
+    assert G.padding_untouched(case, D, SENT[a_type])
+    want = W.encode(G.oracle_ref(case, inp), a_type).reshape(M, N)
+    assert np.array_equal(W.d_logical(case, D), want)
+
+
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("K", [8, 200, 1000])
+def test_row_major_b_ragged_k_bit_exact(K, variant):
+    """N-contiguous B with K a multiple of 8 but not of 64: B's rows past K
+    lie past its record count, A's chunks past K read from past every
+    record."""
+    M, N = 300, 520
+    case = W.GemmCase(name="ragged_k_nn", M=M, N=N, K=K, a_type=W.BF16, b_type=W.BF16,
+                      d_type=W.BF16, b_order=W.ROW, alpha=1.5, beta=0.5, act=W.ACT_RELU,
+                      has_c=True, has_bias=True, seed=K + 7 * variant, dist_a="int3",
+                      dist_b="int3", dist_c="int3", dist_bias="eighths")
+    case.lda += 8
+    case.ldb += 16
+    assert G.variant(case) == "gemm_fast_128x128"
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT[W.BF16], variant=variant)
+    assert G.padding_untouched(case, D, SENT[W.BF16])
+    want = W.encode(G.oracle_ref(case, inp), W.BF16).reshape(M, N)
+    assert np.array_equal(W.d_logical(case, D), want)
+
+
+def test_ragged_k_random_4096_auto():
+    """bf16 4096 x 4096 x 4000 (K ends inside the last 64-element slab) on
+    the automatically chosen two-group kernel, random inputs, sampled
+    against the oracle."""
+    case = _small(M=4096, N=4096, K=4000, act=W.ACT_RELU, seed=23)
+    assert G.variant(case) == "gemm_pingpong_256x256"
+    _check_sampled(case, W.gemm_inputs(case), seed=5)
+
+
 def test_c_aliases_d():
     case = _small(M=200, N=136, K=64)
     inp = W.gemm_inputs(case)

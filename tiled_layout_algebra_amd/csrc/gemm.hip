@@ -117,7 +117,8 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
   schedule(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int wm0 = (wave % kWM) * WM, wn0 = (wave / kWM) * WN;
-  const int KT = p.K / BK;
+  const int KT = (p.K + BK - 1) / BK;
+  const int KTf = p.K / BK;  // whole k-tiles; tile KTf, if K ends inside it, is ragged
 
   // Copy q (A for q < IA, else B): slab row r = tid/kChunks + (NT/kChunks)*q',
   // landing at slab slot wave*64 + NT*q' (lane-linear); the lane fetches the
@@ -162,6 +163,22 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
     });
   }
   const int x_records = kConv ? (int)((int64_t)p.M / (p.cP * p.cQ) * p.cH * p.cW * p.cC * EB) : 0;
+  // The ragged last k-tile (K a multiple of the 16-byte chunk): bit q is set
+  // when copy q's K-contiguous chunk lies past K -- that copy then reads from
+  // past every record and the range check returns zeros.  An N-contiguous B
+  // slab's rows past K lie past its record count (K rows).
+  uint32_t tail_past = 0;
+  if constexpr (!kConv) {
+    static_for<kLoads>([&](auto q) {
+      constexpr bool kA = q < IA;
+      constexpr int qq = kA ? q : q - IA;
+      if constexpr (kA || !kBT) {
+        const int r = tid / kChunks + (NT / kChunks) * qq;
+        if (Swz::chunk(r, tid % kChunks) * 16 >= (p.K - KTf * BK) * EB) tail_past |= 1u << q;
+      }
+    });
+  }
+  const int b_records = kBT ? (int)min((int64_t)p.K * p.b_sk * EB, (int64_t)0x7FFFFFFF) : 0;
   // Fragment bases for each k-step (and each 16-byte half of a 32-byte
   // fragment): row wm0 + lane%32 of the A slot, wn0 + lane%32 of the B slot.
   uint32_t fa[KSTEPS][kSub], fb[KSTEPS][kSub];
@@ -219,7 +236,9 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
   };
   // copy q of tile t into slot `slot`; tiles past K reload the last one
   auto copy = [&](int t, auto slot, auto q) {
-    const uint32_t kb = (uint32_t)min(t, KT - 1) * kRowBytes;
+    const int tt = min(t, KT - 1);
+    const uint32_t kb = (uint32_t)tt * kRowBytes;
+    const uint32_t o = (tt == KTf && ((tail_past >> q) & 1)) ? 0x80000000u : off[q];
     if constexpr (q < IA && kConv) {
       const int k0 = min(t, KT - 1) * BK;  // first channel of the tap, uniform
       const int rs = k0 / p.cC, c0 = k0 - rs * p.cC;
@@ -234,12 +253,12 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
       dma16_buf(p.A, in ? off[q] + tap : 0xFFFFFFF0u, 0,
                 smem + slot * SLAB_A + (wave * 64 + NT * q) * 16, x_records);
     } else if constexpr (q < IA)
-      dma16_buf(p.A, off[q], kb, smem + slot * SLAB_A + (wave * 64 + NT * q) * 16);
+      dma16_buf(p.A, o, kb, smem + slot * SLAB_A + (wave * 64 + NT * q) * 16);
     else if constexpr (kBT)
-      dma16_buf(p.B, off[q], (uint32_t)(min(t, KT - 1) * BK) * (uint32_t)(p.b_sk * EB),
-                smem + B_BASE + slot * SLAB_B + (wave * 64 + NT * (q - IA)) * 16);
+      dma16_buf(p.B, off[q], (uint32_t)(tt * BK) * (uint32_t)(p.b_sk * EB),
+                smem + B_BASE + slot * SLAB_B + (wave * 64 + NT * (q - IA)) * 16, b_records);
     else
-      dma16_buf(p.B, off[q], kb, smem + B_BASE + slot * SLAB_B + (wave * 64 + NT * (q - IA)) * 16);
+      dma16_buf(p.B, o, kb, smem + B_BASE + slot * SLAB_B + (wave * 64 + NT * (q - IA)) * 16);
   };
   // MFMAs [lo, hi) of a step with copies [q0, q0 + nq) of tile t spread
   // evenly between them: after MFMA k come copies [k*nq/n, (k+1)*nq/n).
@@ -328,7 +347,9 @@ int launch_fast(const GemmParams& p0, hipStream_t stream) {
 
 // The variants the library ships.  Every fast variant moves whole 128-byte
 // K rows per copy (the direct-to-LDS copy rate per compute unit halves with
-// every halving of the row width), so K must be a multiple of 128 bytes.
+// every halving of the row width).  With 16-bit operands K need only be a
+// multiple of the 16-byte chunk: the last k-tile's chunks past K read zeros
+// through the buffer range check; e4m3 needs whole 128-byte rows.
 //   0 two-group 256x256 kernel (gemm_pingpong.hip), any operand type: two
 //     groups of four wavefronts (2x2 waves of 64x128 each) alternate
 //     between MFMA-only and memory phases.
@@ -556,12 +577,16 @@ int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const 
   // the fast kernel addresses each operand with 32-bit offsets below 2^31
   const bool small_ops = (int64_t)g.M * g.lda * eb < (int64_t(1) << 31) &&
                          (int64_t)g.N * g.ldb * eb < (int64_t(1) << 31);
-  const bool fast = a_vec && b_vec && small_ops && g.K > 0 && (g.K % BK) == 0;
+  // K: whole 128-byte slabs for e4m3 (its 128 x 128 and 256 x 256 kernels
+  // copy without a range check); for 16-bit operands any multiple of the
+  // 16-byte chunk -- the last k-tile's chunks past K read zeros
+  const bool k_ok = g.K > 0 && (eb == 1 ? (g.K % BK) == 0 : (g.K % (16 / eb)) == 0);
+  const bool fast = a_vec && b_vec && small_ops && k_ok;
   // A in the fast layout, B a 16-bit row-major K x N matrix with 16-byte
   // aligned rows and whole 16-byte chunks of columns, below 2 GiB
   const bool bt = !fast && nt && a_vec && b_rows16 && g.N % 8 == 0 &&
                   (int64_t)g.M * g.lda * eb < (int64_t(1) << 31) &&
-                  (int64_t)g.K * g.ldb * eb < (int64_t(1) << 31) && g.K > 0 && (g.K % BK) == 0;
+                  (int64_t)g.K * g.ldb * eb < (int64_t(1) << 31) && k_ok;
   const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256);
   const bool big = tiles256 >= 128;
   switch (g.a_type) {

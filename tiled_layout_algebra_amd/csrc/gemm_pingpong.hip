@@ -83,7 +83,8 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   schedule(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int wm0 = 128 * grp + WM * (wave & 1), wn0 = WN * ((wave >> 1) & 1);
-  const int KT = p.K / BK;
+  const int KT = (p.K + BK - 1) / BK;
+  const int KTf = p.K / BK;  // whole k-tiles; tile KTf, if K ends inside it, is ragged
 
   // ---- copies: group 0 moves A (two LDS slots), group 1 moves B (three
   // slots), 8 instructions per slab.  Thread t fills slot byte 16 (t + 256q)
@@ -120,6 +121,14 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
       static_for<kCopies>([&](auto q) { recs[q] = (int)min(whole, (int64_t)0x7FFFFFFF); });
     }
   }
+  // The ragged last k-tile (K a multiple of the 16-byte chunk): a lane whose
+  // K-contiguous chunk lies past K reads from past every record, so the
+  // range check returns zeros; an N-contiguous B slab's rows past K are
+  // past its records already.
+  uint32_t voff_tail = voff;
+  if (grp == 0 || !kBT) {
+    if (Swz::chunk(r0, t % kChunks) * 16 >= (p.K - KTf * BK) * EB) voff_tail = 0x80000000u;
+  }
   // Copy q of k-tile kt into `slot`.  A copy past the last k-tile still runs
   // (so the instruction stream and the wait counts never change) but with no
   // records: it writes zeros into a slot nobody reads any more.
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(smem + lds_op + slot * SLAB + q * 4096 +
                                                      (wave & 3) * 1024),
-        16, voff, (uint32_t)kt * kt_bytes + (uint32_t)q * q_bytes, 0, 0);
+        16, kt == KTf ? voff_tail : voff, (uint32_t)kt * kt_bytes + (uint32_t)q * q_bytes, 0, 0);
   };
   auto copy_slab = [&](int kt, int slot, bool live) {
     static_for<kCopies>([&](auto q) { copy_one(kt, slot, live, q); });

@@ -129,7 +129,7 @@ def probe_source():
     body = _edit(body, "void gemm_pingpong_kernel(const GemmParams p) {",
                  "void gemm_pingpong_kernel(const GemmParams p, uint64_t* __restrict__ stamps,\n"
                  "                                              uint64_t* __restrict__ rtime) {")
-    body = _edit(body, "  const int KT = p.K / BK;\n", """  const int KT = p.K / BK;
+    body = _edit(body, "  const int KT = (p.K + BK - 1) / BK;\n", """  const int KT = (p.K + BK - 1) / BK;
   uint64_t* const st_ = stamps + (size_t)(blockIdx.x * 8 + wave) * MAX_STAMPS;
   int ts_ = 0;
   auto stamp = [&]() {
