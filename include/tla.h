@@ -138,10 +138,9 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  *                            ragged K
  *   3 "gemm_fast_256x256"    256x256 tiles, one group (16-bit: 8 wavefronts
  *                            of 128x64; e4m3: 4 of 128x128), direct copies
- * tla_gemm_epilogue picks one from the problem: in the fast layout,
- * variant 0 with at least 128 tiles of 256x256 and 1 otherwise; in the
- * N-contiguous-B layout, variant 0 with at least 256 tiles of 256x256 and 1
- * otherwise; variant 2 outside both;
+ * tla_gemm_epilogue picks one from the problem: in the fast layout and in
+ * the N-contiguous-B layout, variant 0 with at least 128 tiles of 256x256
+ * and 1 otherwise; variant 2 outside both;
  * tla_gemm_run_variant runs the one asked for, with the same semantics and
  * tolerance, or returns TLA_ERR_UNSUPPORTED when a fast variant is asked
  * for a problem without the fast layout (both operands K-contiguous,

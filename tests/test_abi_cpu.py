@@ -100,14 +100,15 @@ def test_gemm_variant_choice():
     # fp8 slabs are 128 elements wide: K = 64 is ragged for e4m3
     assert _variant(_args(**dict(e4, K=64, lda=64, ldb=64)))[1] == "gemm_general_128x128"
     # N-contiguous 16-bit B with aligned rows: the 128 x 128 transpose-read
-    # kernel below 256 tiles of 256 x 256, the two-group kernel's
-    # transpose-read form from there on
+    # kernel below 128 tiles of 256 x 256, the two-group kernel's
+    # transpose-read form from there on (the fast layout's rule)
     assert _variant(_args(b_order=tla.ROW_MAJOR))[1] == "gemm_fast_128x128"
     big_nn = dict(M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldd=4096, b_order=tla.ROW_MAJOR)
     assert _variant(_args(**big_nn))[1] == "gemm_pingpong_256x256"
-    assert _variant(_args(**dict(big_nn, M=3072, N=3072, ldb=3072, ldd=3072)))[1] == "gemm_fast_128x128"
-    assert _variant(_args(**dict(big_nn, M=4096 - 256)))[1] == "gemm_fast_128x128"  # 240 tiles
-    assert _variant(_args(**dict(big_nn, M=4096 - 255)))[1] == "gemm_pingpong_256x256"  # 256
+    assert _variant(_args(**dict(big_nn, M=3072, N=3072, ldb=3072, ldd=3072)))[1] == "gemm_pingpong_256x256"
+    assert _variant(_args(**dict(big_nn, M=2048, N=2048, ldb=2048, ldd=2048)))[1] == "gemm_fast_128x128"
+    assert _variant(_args(**dict(big_nn, M=2048 - 256)))[1] == "gemm_fast_128x128"  # 112 tiles
+    assert _variant(_args(**dict(big_nn, M=2048)))[1] == "gemm_pingpong_256x256"  # 128
     # ... but not for e4m3, N not a multiple of 8, unaligned B rows or K off
     # the 16-byte chunk
     assert _variant(_args(**dict(e4, b_order=tla.ROW_MAJOR)))[1] == "gemm_general_128x128"

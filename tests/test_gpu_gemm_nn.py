@@ -7,7 +7,7 @@ the oracle:
   epilogue (alpha, beta*C, bias, ReLU), ragged M and N (N a multiple of 8,
   down to one 16-byte chunk), K from one k-tile up, and pitched operands
   with NaN padding;
-* the kernel choice: variant 1 below 256 tiles of 256 x 256, variant 0
+* the kernel choice: variant 1 below 128 tiles of 256 x 256, variant 0
   (its own transpose-read form) from there on, either forcible, variant 3
   refused, the general kernel forcible;
 * the general kernel's own k-rows-of-n slab for pitches and bases off

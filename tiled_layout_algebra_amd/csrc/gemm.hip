@@ -372,14 +372,12 @@ const int kVariantTile[kGemmVariants] = {256, 128, 128, 256};
 template <int kCode>
 int dispatch_typed(const GemmParams& p, bool fast, bool bt, bool big, hipStream_t s, bool dry,
                    const char** name, int forced) {
-  // N-contiguous B: the two-group kernel's transpose-read form once there
-  // are 256 tiles of 256 x 256 (one per CU), the 128 x 128 kernel below
-  // (bf16, four alternating rounds, medians: 4096^3 with C, bias and ReLU
-  // 129.9 against 135.2 us, 8192^2 x 2048 258.0 against 277.9 us, 4096 x
-  // 8192 x 4096 244.8 against 257.9 us; 3072^2 x 4096, 144 tiles, 112.4
-  // against 88.8 us, 2048^3 54.5 against 19.5 us)
-  const bool full_round = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) >= 256;
-  const int v = forced >= 0 ? forced : (fast ? (big ? 0 : 1) : (bt ? (full_round ? 0 : 1) : 2));
+  // N-contiguous B: the two-group kernel's transpose-read form from 128 tiles
+  // of 256 x 256 on, as in the fast layout, the 128 x 128 kernel below (bf16,
+  // four alternating rounds, medians: 4096^3 with C, bias and ReLU 109.4
+  // against 139.3 us, 8192^2 x 2048 213.7 against 283.5 us, 3072^2 x 4096,
+  // 144 tiles, 79.9 against 91.9 us; 2048^3 38.8 against 20.1 us)
+  const int v = forced >= 0 ? forced : ((fast || bt) ? (big ? 0 : 1) : 2);
   // a fast variant needs the fast layout (variants 0 and 1 also take `bt`)
   if (v != 2 && !fast && !(v <= 1 && bt)) return TLA_ERR_UNSUPPORTED;
   if (name) *name = kVariantNames[v];
