@@ -144,11 +144,13 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  * tla_gemm_run_variant runs the one asked for, with the same semantics and
  * tolerance, or returns TLA_ERR_UNSUPPORTED when a fast variant is asked
  * for a problem without the fast layout (both operands K-contiguous,
- * 16-byte aligned rows, K a multiple of 8 for 16-bit operands -- the last
- * k-tile may end inside the 64-element slab -- or of 128 for e4m3, each
- * operand < 2 GiB) -- variants 0 and 1 also accept the N-contiguous-B layout
- * (16-bit operands; A as in the fast layout; B row-major with 16-byte
- * aligned rows, N and K multiples of 8, B below 2 GiB).
+ * 16-byte aligned rows, K a multiple of 8 for 16-bit operands or of 16 for
+ * e4m3 -- the last k-tile may end inside the slab -- each operand < 2 GiB;
+ * e4m3 variants 1 and 3 need K a multiple of 128, and the automatic choice
+ * for e4m3 below 128 tiles with other K is variant 2) -- variants 0 and 1
+ * also accept the N-contiguous-B layout (16-bit operands; A as in the fast
+ * layout; B row-major with 16-byte aligned rows, N and K multiples of 8, B
+ * below 2 GiB).
  * Variant ids outside [0, TLA_GEMM_VARIANTS) are TLA_ERR_INVALID_ARG.
  */
 #define TLA_GEMM_VARIANTS 4

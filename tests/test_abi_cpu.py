@@ -97,8 +97,11 @@ def test_gemm_variant_choice():
     e4 = dict(a_type=tla.E4M3, b_type=tla.E4M3, M=8192, N=8192, K=8192, lda=8192, ldb=8192, ldd=8192)
     assert _variant(_args(**e4))[1] == "gemm_pingpong_256x256"
     assert _variant(_args(**dict(e4, M=1024, N=1024)))[1] == "gemm_fast_128x128"
-    # fp8 slabs are 128 elements wide: K = 64 is ragged for e4m3
-    assert _variant(_args(**dict(e4, K=64, lda=64, ldb=64)))[1] == "gemm_general_128x128"
+    # fp8 slabs are 128 elements wide: with K = 64 only the two-group kernel
+    # (range-checked copies) stays fast, so small e4m3 problems go general
+    assert _variant(_args(**dict(e4, K=64, lda=64, ldb=64)))[1] == "gemm_pingpong_256x256"
+    assert _variant(_args(**dict(e4, M=1024, N=1024, K=64, lda=64, ldb=64)))[1] == "gemm_general_128x128"
+    assert _variant(_args(**dict(e4, K=72, lda=80, ldb=80)))[1] == "gemm_general_128x128"  # K % 16
     # N-contiguous 16-bit B with aligned rows: the 128 x 128 transpose-read
     # kernel below 128 tiles of 256 x 256, the two-group kernel's
     # transpose-read form from there on (the fast layout's rule)
@@ -250,6 +253,11 @@ def test_run_variant_argument_errors():
     # aligned N-contiguous B: the single-group 256 x 256 kernel has no such form
     nn = _args(b_order=tla.ROW_MAJOR, ldb=64)
     assert tla.lib().tla_gemm_run_variant(ctypes.byref(nn), 3, None) == tla.ERR_UNSUPPORTED
+    # e4m3 with K off the 128-byte slab: the 128 x 128 and 256 x 256 kernels
+    # copy whole slabs without a range check
+    e4 = _args(a_type=tla.E4M3, b_type=tla.E4M3, K=80, lda=80, ldb=80)
+    for v in (1, 3):
+        assert tla.lib().tla_gemm_run_variant(ctypes.byref(e4), v, None) == tla.ERR_UNSUPPORTED
 
 
 def _conv(**kw):

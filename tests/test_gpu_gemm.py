@@ -348,6 +348,27 @@ def test_row_major_b_ragged_k_bit_exact(K, variant):
     assert np.array_equal(W.d_logical(case, D), want)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 520, 144), (4096, 2048, 80)])
+def test_e4m3_ragged_k_two_group_bit_exact(M, N, K):
+    """e4m3 with K a multiple of 16 but not of the 128-element slab: the
+    two-group kernel (chosen from 128 tiles of 256 x 256, forced below) reads
+    zeros past K through its range-checked copies; the pitches carry NaN
+    padding right past K."""
+    case = W.GemmCase(name="e4_ragged_k", M=M, N=N, K=K, a_type=W.E4M3, b_type=W.E4M3,
+                      d_type=W.BF16, alpha=1.5, beta=0.5, act=W.ACT_RELU, has_c=True,
+                      has_bias=True, seed=K + M, dist_a="int3", dist_b="int3",
+                      dist_c="int3", dist_bias="eighths")
+    case.lda += 16
+    case.ldb += 16
+    big = (M // 256) * (N // 256) >= 128
+    assert G.variant(case) == ("gemm_pingpong_256x256" if big else "gemm_general_128x128")
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT[W.BF16], variant=None if big else 0)
+    assert G.padding_untouched(case, D, SENT[W.BF16])
+    want = W.encode(G.oracle_ref(case, inp), W.BF16).reshape(M, N)
+    assert np.array_equal(W.d_logical(case, D), want)
+
+
 def test_ragged_k_random_4096_auto():
     """bf16 4096 x 4096 x 4000 (K ends inside the last 64-element slab) on
     the automatically chosen two-group kernel, random inputs, sampled

@@ -347,9 +347,10 @@ int launch_fast(const GemmParams& p0, hipStream_t stream) {
 
 // The variants the library ships.  Every fast variant moves whole 128-byte
 // K rows per copy (the direct-to-LDS copy rate per compute unit halves with
-// every halving of the row width).  With 16-bit operands K need only be a
-// multiple of the 16-byte chunk: the last k-tile's chunks past K read zeros
-// through the buffer range check; e4m3 needs whole 128-byte rows.
+// every halving of the row width).  K need only be a multiple of the 16-byte
+// chunk: the last k-tile's chunks past K read zeros through the buffer range
+// check -- except in e4m3's 128 x 128 and 256 x 256 kernels, which copy
+// through global_load_lds and need whole 128-byte rows.
 //   0 two-group 256x256 kernel (gemm_pingpong.hip), any operand type: two
 //     groups of four wavefronts (2x2 waves of 64x128 each) alternate
 //     between MFMA-only and memory phases.
@@ -370,16 +371,22 @@ const int kVariantTile[kGemmVariants] = {256, 128, 128, 256};
 // 16-byte chunks of n): variant 1's kernel takes B through LDS transpose
 // reads.
 template <int kCode>
-int dispatch_typed(const GemmParams& p, bool fast, bool bt, bool big, hipStream_t s, bool dry,
-                   const char** name, int forced) {
+int dispatch_typed(const GemmParams& p, bool fast, bool bt, bool big, bool k_slab, hipStream_t s,
+                   bool dry, const char** name, int forced) {
   // N-contiguous B: the two-group kernel's transpose-read form from 128 tiles
   // of 256 x 256 on, as in the fast layout, the 128 x 128 kernel below (bf16,
   // four alternating rounds, medians: 4096^3 with C, bias and ReLU 109.4
   // against 139.3 us, 8192^2 x 2048 213.7 against 283.5 us, 3072^2 x 4096,
   // 144 tiles, 79.9 against 91.9 us; 2048^3 38.8 against 20.1 us)
-  const int v = forced >= 0 ? forced : ((fast || bt) ? (big ? 0 : 1) : 2);
+  int v = forced >= 0 ? forced : ((fast || bt) ? (big ? 0 : 1) : 2);
   // a fast variant needs the fast layout (variants 0 and 1 also take `bt`)
   if (v != 2 && !fast && !(v <= 1 && bt)) return TLA_ERR_UNSUPPORTED;
+  // e4m3's 128 x 128 and 256 x 256 kernels copy whole 128-byte slabs with no
+  // range check: K off the slab takes the two-group kernel or the general one
+  if constexpr (kCode == kE4M3) {
+    if (!k_slab && v == 1 && forced < 0) v = 2;
+    if (!k_slab && (v == 1 || v == 3)) return TLA_ERR_UNSUPPORTED;
+  }
   if (name) *name = kVariantNames[v];
   if (dry) return TLA_OK;
   if constexpr (kCode != kE4M3) {
@@ -575,10 +582,10 @@ int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const 
   // the fast kernel addresses each operand with 32-bit offsets below 2^31
   const bool small_ops = (int64_t)g.M * g.lda * eb < (int64_t(1) << 31) &&
                          (int64_t)g.N * g.ldb * eb < (int64_t(1) << 31);
-  // K: whole 128-byte slabs for e4m3 (its 128 x 128 and 256 x 256 kernels
-  // copy without a range check); for 16-bit operands any multiple of the
-  // 16-byte chunk -- the last k-tile's chunks past K read zeros
-  const bool k_ok = g.K > 0 && (eb == 1 ? (g.K % BK) == 0 : (g.K % (16 / eb)) == 0);
+  // K: any multiple of the 16-byte chunk -- the last k-tile's chunks past K
+  // read zeros (e4m3 off the 128-byte slab: the two-group kernel only)
+  const bool k_ok = g.K > 0 && (g.K % (16 / eb)) == 0;
+  const bool k_slab = g.K > 0 && (g.K % BK) == 0;
   const bool fast = a_vec && b_vec && small_ops && k_ok;
   // A in the fast layout, B a 16-bit row-major K x N matrix with 16-byte
   // aligned rows and whole 16-byte chunks of columns, below 2 GiB
@@ -588,9 +595,12 @@ int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const 
   const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256);
   const bool big = tiles256 >= 128;
   switch (g.a_type) {
-    case TLA_BF16: return dispatch_typed<kBF16>(p, fast, bt, big, stream, dry_run, name, forced);
-    case TLA_F16: return dispatch_typed<kF16>(p, fast, bt, big, stream, dry_run, name, forced);
-    case TLA_E4M3: return dispatch_typed<kE4M3>(p, fast, false, big, stream, dry_run, name, forced);
+    case TLA_BF16:
+      return dispatch_typed<kBF16>(p, fast, bt, big, k_slab, stream, dry_run, name, forced);
+    case TLA_F16:
+      return dispatch_typed<kF16>(p, fast, bt, big, k_slab, stream, dry_run, name, forced);
+    case TLA_E4M3:
+      return dispatch_typed<kE4M3>(p, fast, false, big, k_slab, stream, dry_run, name, forced);
     default: return TLA_ERR_UNSUPPORTED;
   }
 }

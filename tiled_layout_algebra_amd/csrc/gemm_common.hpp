@@ -47,9 +47,9 @@ struct GemmParams {
 
 // The two-group 256 x 256 kernel of gemm_pingpong.hip for 16-bit or e4m3
 // operands in the fast layout (both operands K-contiguous with 16-byte
-// aligned rows, K a multiple of 16 bytes -- of 128 for e4m3 -- each
-// operand below 2 GiB); with `bt`, 16-bit operands whose B is N-contiguous
-// instead (16-byte aligned rows, N a multiple of 8).
+// aligned rows, K a multiple of 16 bytes, each operand below 2 GiB); with
+// `bt`, 16-bit operands whose B is N-contiguous instead (16-byte aligned
+// rows, N a multiple of 8).
 int launch_pingpong(const GemmParams& p, int a_type, hipStream_t stream, bool bt = false);
 const void* pingpong_kernel(int a_type);
 
