@@ -2,11 +2,12 @@
 // (BM/2) x (BN/2), two LDS stages) for gfx950, in two forms:
 //
 //   register-staged  the general path: any order, pitch or alignment of A
-//                    and B, ragged K.  Each thread loads its chunks of the
-//                    next k-tile into registers before the MFMAs of the
-//                    current one and writes them to the other LDS stage
-//                    after them.  Elements outside the matrix load as zero.
-//                    Also the implicit-GEMM convolution's fallback loader.
+//                    and B, ragged K.  Each thread loads its chunks of a
+//                    k-tile into registers before the MFMAs of an earlier
+//                    one (two tiles ahead inside K) and writes them to the
+//                    other LDS stage after the MFMAs of the tile before it.
+//                    Elements outside the matrix load as zero.  Also the
+//                    implicit-GEMM convolution's fallback loader.
 //   direct-to-LDS    e4m3 in the fast layout (variants 1 and 3).
 //
 //   D = act(alpha_eff * A.B + beta*C + bias),  fp32 accumulation.
@@ -171,11 +172,11 @@ __global__ __launch_bounds__(kThreads, (kFast || (!kAKC && elem_bytes(kCode) != 
     };
     static_assert(!kConv || !kFast, "the convolution view uses the register-staged path");
     // Two register sets per operand.  Tiles 0 .. KTw - 1 lie inside K; they
-    // load as whole chunks with no per-lane branch, two tiles ahead: tile t + 2 goes into set t % 2
-    // before the MFMAs of tile t, and set (t + 1) % 2 (tile t + 1, loaded a
-    // whole iteration earlier) is written to the other LDS stage after them.
-    // The ragged rest goes one tile ahead through the element-wise loader.
-    // Tile t lives in LDS stage t % 2.
+    // load as whole chunks with no per-lane branch, two tiles ahead: tile
+    // t + 2 goes into set t % 2 before the MFMAs of tile t, and set
+    // (t + 1) % 2 (tile t + 1, loaded a whole iteration earlier) is written
+    // to the other LDS stage after them.  The ragged rest goes one tile
+    // ahead through the edge loader.  Tile t lives in LDS stage t % 2.
     using RA = std::conditional_t<
         kConv, ConvSlab<BM, EB, kRowBytes>,
         std::conditional_t<kAT, RegSlabNT<BM, BK>, RegSlab<BM, EB, kRowBytes, kAKC>>>;
