@@ -131,8 +131,9 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  *   1 "gemm_fast_128x128"    128x128 tiles, direct copies (16-bit: 8
  *                            wavefronts of 64x32; e4m3: 4 of 64x64); for
  *                            16-bit operands B may also be N-contiguous
- *                            (row-major K x N): its fragments are then read
- *                            through LDS transpose reads
+ *                            (row-major K x N) and A M-contiguous
+ *                            (column-major M x K): their fragments are then
+ *                            read through LDS transpose reads
  *   2 "gemm_general_128x128" 128x128 tiles, 4 wavefronts, register-staged
  *                            predicated loads: any order, pitch, alignment,
  *                            ragged K
@@ -140,7 +141,8 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  *                            of 128x64; e4m3: 4 of 128x128), direct copies
  * tla_gemm_epilogue picks one from the problem: in the fast layout and in
  * the N-contiguous-B layout, variant 0 with at least 128 tiles of 256x256
- * and 1 otherwise; variant 2 outside both;
+ * and 1 otherwise; in the M-contiguous-A layout variant 1; variant 2
+ * outside them;
  * tla_gemm_run_variant runs the one asked for, with the same semantics and
  * tolerance, or returns TLA_ERR_UNSUPPORTED when a fast variant is asked
  * for a problem without the fast layout (both operands K-contiguous,
@@ -150,7 +152,9 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  * for e4m3 below 128 tiles with other K is variant 2) -- variants 0 and 1
  * also accept the N-contiguous-B layout (16-bit operands; A as in the fast
  * layout; B row-major with 16-byte aligned rows, N and K multiples of 8, B
- * below 2 GiB).
+ * below 2 GiB), and variant 1 the M-contiguous-A layout (16-bit operands; A
+ * column-major with 16-byte aligned columns, M and K multiples of 8, A
+ * below 2 GiB; B in either of the layouts above).
  * Variant ids outside [0, TLA_GEMM_VARIANTS) are TLA_ERR_INVALID_ARG.
  */
 #define TLA_GEMM_VARIANTS 4

@@ -282,6 +282,35 @@ def test_column_major_a_bit_exact(M, N, K, a_type, b_order):
 
 @pytest.mark.parametrize("b_order", [W.ROW, W.COL])
 @pytest.mark.parametrize("a_type", [W.F16, W.BF16])
+@pytest.mark.parametrize("M,N,K", [(296, 264, 200), (8, 40, 64), (1024, 520, 1000)])
+def test_column_major_a_fast_kernel_bit_exact(M, N, K, a_type, b_order):
+    """A column-major with 16-byte aligned columns and M a multiple of 8: the
+    128 x 128 kernel holds A as k rows of m (direct copies, transpose reads);
+    rows of k past K lie past the copy's record count, tiles past M read the
+    last 8 columns; NaN pitch padding on every operand; integer inputs, so D
+    is exact."""
+    case = W.GemmCase(name="acol_fast", M=M, N=N, K=K, a_type=a_type, b_type=a_type,
+                      d_type=a_type, a_order=W.COL, b_order=b_order, alpha=1.5, beta=0.5,
+                      act=W.ACT_RELU, has_c=True, has_bias=True, seed=M + N + K + 1,
+                      dist_a="int3", dist_b="int3", dist_c="int3", dist_bias="eighths")
+    case.lda += 8
+    case.ldb += 8 if b_order == W.COL else 16
+    assert G.variant(case) == "gemm_fast_128x128"
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT[a_type])
+    assert G.padding_untouched(case, D, SENT[a_type])
+    want = W.encode(G.oracle_ref(case, inp), a_type).reshape(M, N)
+    assert np.array_equal(W.d_logical(case, D), want)
+
+
+def test_column_major_a_fast_kernel_random_2048():
+    case = _small(M=2048, N=2048, K=1024, a_order=W.COL, act=W.ACT_GELU, seed=24)
+    assert G.variant(case) == "gemm_fast_128x128"
+    _check_full(case, W.gemm_inputs(case))
+
+
+@pytest.mark.parametrize("b_order", [W.ROW, W.COL])
+@pytest.mark.parametrize("a_type", [W.F16, W.BF16])
 @pytest.mark.parametrize("M,N,K", [(130, 201, 96), (70, 4223, 64), (257, 69, 40), (65, 4129, 16)])
 def test_odd_pitch_epilogue_edges_bit_exact(M, N, K, a_type, b_order):
     """C and D at odd pitches with a bias: wave tiles that end inside M, or

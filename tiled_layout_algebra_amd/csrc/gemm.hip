@@ -70,8 +70,13 @@ namespace {
 // + 3, and lane j receives B[k0 .. k0 + 3][n0 + j].  The swizzle keeps the
 // 32 lanes of one half-wave (rows k0 .. k0 + 3, 32 bytes each of two
 // column groups) on 16 distinct 16-byte bank groups.
+//
+// kAT: A is M-contiguous (a column-major M x K matrix, 16-bit, M a multiple
+// of 8), held the same way: BK rows of k, each BM columns of m, an A
+// fragment two transpose reads per 32 rows of m (an A fragment has a B
+// fragment's layout).  Rows of k past K lie past the copy's record count.
 template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront = 0, int kWM = 2,
-          int kWN = 2, bool kConv = false, bool kBT = false>
+          int kWN = 2, bool kConv = false, bool kBT = false, bool kAT = false>
 __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmParams p) {
   using Atom = MfmaAtom<kCode>;
   using Frag = typename Atom::Frag;
@@ -90,8 +95,11 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
   static_assert(kStages * (SLAB_A + SLAB_B) <= 160 * 1024, "LDS budget");
   static_assert(!kBT || (EB == 2 && BN >= 128 && !kConv && kWN * 32 == BN),
                 "N-contiguous B: 16-bit, one 32-column fragment per wave");
+  static_assert(!kAT || (EB == 2 && BM >= 128 && !kConv), "M-contiguous A: 16-bit");
   constexpr int kRowBT = BN * 2;                   // bytes per k row of an N-contiguous slab
   constexpr int kChBT = kRowBT / 16;
+  constexpr int kRowAT = BM * 2;                   // bytes per k row of an M-contiguous slab
+  constexpr int kChAT = kRowAT / 16;
   static_assert(kStages * SLAB_A <= 65536 && kStages * SLAB_B <= 65536, "fragment immediates");
   constexpr int kChunks = Slab<kRowBytes>::kChunks;
   static_assert((1 << Slab<kRowBytes>::kRowShift) * kChunks <= 32, "swizzle period divides 32 rows");
@@ -99,7 +107,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
   static_assert(IA * NT == BM * kChunks && IB * NT == BN * kChunks, "whole copy instructions");
   constexpr int kLoads = IA + IB;                  // copies per thread per tile
   constexpr int kSub = Atom::kLaneBytes / 16;      // 16-byte reads per fragment
-  constexpr int kReads = FM * kSub + (kBT ? 2 : FN * kSub);
+  constexpr int kReads = (kAT ? 2 * FM : FM * kSub) + (kBT ? 2 : FN * kSub);
   constexpr int kMfmas = FM * FN;
   constexpr int kStepBytes = Atom::kK * EB;
   // Copies per full step, the rest go into the first half of the last step.
@@ -128,7 +136,13 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
   static_for<kLoads>([&](auto q) {
     constexpr bool kA = q < IA;
     constexpr int qq = kA ? q : q - IA;
-    if constexpr (!kA && kBT) {
+    if constexpr (kA && kAT) {
+      // as for an N-contiguous B: k row r, stored chunk pc holding columns
+      // m0 + 8 (pc ^ 4 (r % 4)) .. + 7, clamped to the last chunk of M
+      const int sc = tid + NT * qq, r = sc / kChAT, pc = sc % kChAT;
+      const int m = min(m0 + 8 * (pc ^ (4 * (r & 3))), p.M - 8);
+      off[q] = (uint32_t)(((int64_t)r * p.a_sk + m) * EB);
+    } else if constexpr (!kA && kBT) {
       // slab chunk tid + NT q': k row r, stored chunk pc, which holds logical
       // chunk pc ^ 4 (r % 4): columns n0 + 8 lc .. + 7, clamped to the last
       // whole chunk of the matrix (columns past N are never stored)
@@ -172,13 +186,14 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
     static_for<kLoads>([&](auto q) {
       constexpr bool kA = q < IA;
       constexpr int qq = kA ? q : q - IA;
-      if constexpr (kA || !kBT) {
+      if constexpr (kA ? !kAT : !kBT) {
         const int r = tid / kChunks + (NT / kChunks) * qq;
         if (Swz::chunk(r, tid % kChunks) * 16 >= (p.K - KTf * BK) * EB) tail_past |= 1u << q;
       }
     });
   }
   const int b_records = kBT ? (int)min((int64_t)p.K * p.b_sk * EB, (int64_t)0x7FFFFFFF) : 0;
+  const int a_records = kAT ? (int)min((int64_t)p.K * p.a_sk * EB, (int64_t)0x7FFFFFFF) : 0;
   // Fragment bases for each k-step (and each 16-byte half of a 32-byte
   // fragment): row wm0 + lane%32 of the A slot, wn0 + lane%32 of the B slot.
   uint32_t fa[KSTEPS][kSub], fb[KSTEPS][kSub];
@@ -205,6 +220,22 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
     });
   }
 
+  // M-contiguous A: the same two reads for each 32-row fragment i (the
+  // swizzle does not commute with the 32-row step, so each has its bases)
+  uint32_t fat[kAT ? KSTEPS : 1][kAT ? FM : 1][2];
+  if constexpr (kAT) {
+    const int qw = lane >> 4, a4 = lane & 15;
+    static_for<KSTEPS>([&](auto ks) {
+      static_for<FM>([&](auto i) {
+        static_for<2>([&](auto h) {
+          const int k = 16 * ks + 8 * (qw >> 1) + 4 * h + (a4 >> 2);
+          const int m = wm0 + 32 * i + 16 * (qw & 1) + 4 * (a4 & 3);
+          fat[ks][i][h] = (uint32_t)(k * kRowAT + (((m >> 3) ^ (4 * (k & 3))) * 16) + (m & 7) * 2);
+        });
+      });
+    });
+  }
+
   f32x16 acc[FM][FN];
   static_for<FM>([&](auto i) { static_for<FN>([&](auto j) { acc[i][j] = f32x16{}; }); });
   Frag a[2][FM], b[2][FN];
@@ -225,7 +256,10 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
     return Frag{l2[0], l2[1], h2[0], h2[1]};
   };
   auto read_frags = [&](auto buf, auto slot, auto ks) {
-    static_for<FM>([&](auto i) { a[buf][i] = lds_frag(fa[ks], slot * SLAB_A + i * 32 * kRowBytes); });
+    if constexpr (kAT)
+      static_for<FM>([&](auto i) { a[buf][i] = lds_frag_t(fat[ks][i], slot * SLAB_A); });
+    else
+      static_for<FM>([&](auto i) { a[buf][i] = lds_frag(fa[ks], slot * SLAB_A + i * 32 * kRowBytes); });
     if constexpr (kBT)
       b[buf][0] = lds_frag_t(fbt[ks], slot * SLAB_B);
     else
@@ -252,7 +286,10 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
                             (uint32_t)c0) * (uint32_t)EB;
       dma16_buf(p.A, in ? off[q] + tap : 0xFFFFFFF0u, 0,
                 smem + slot * SLAB_A + (wave * 64 + NT * q) * 16, x_records);
-    } else if constexpr (q < IA)
+    } else if constexpr (q < IA && kAT)
+      dma16_buf(p.A, off[q], (uint32_t)(tt * BK) * (uint32_t)(p.a_sk * EB),
+                smem + slot * SLAB_A + (wave * 64 + NT * q) * 16, a_records);
+    else if constexpr (q < IA)
       dma16_buf(p.A, o, kb, smem + slot * SLAB_A + (wave * 64 + NT * q) * 16);
     else if constexpr (kBT)
       dma16_buf(p.B, off[q], (uint32_t)(tt * BK) * (uint32_t)(p.b_sk * EB),
@@ -332,7 +369,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_fast_kernel(const GemmPar
 
 // ----------------------------------------------------------------- dispatch
 template <int kCode, int BM, int BN, int kRowBytes, int kStages, int kFront, int kWM, int kWN,
-          bool kConv = false, bool kBT = false>
+          bool kConv = false, bool kBT = false, bool kAT = false>
 int launch_fast(const GemmParams& p0, hipStream_t stream) {
   GemmParams p = p0;
   int64_t grid;
@@ -340,7 +377,7 @@ int launch_fast(const GemmParams& p0, hipStream_t stream) {
   if (grid <= 0) return TLA_OK;
   if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((gemm_fast_kernel<kCode, BM, BN, kRowBytes, kStages, kFront, kWM, kWN, kConv,
-                                       kBT>),
+                                       kBT, kAT>),
                      dim3((unsigned)grid), dim3(64 * kWM * kWN), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
 }
@@ -371,16 +408,18 @@ const int kVariantTile[kGemmVariants] = {256, 128, 128, 256};
 // 16-byte chunks of n): variant 1's kernel takes B through LDS transpose
 // reads.
 template <int kCode>
-int dispatch_typed(const GemmParams& p, bool fast, bool bt, bool big, bool k_slab, hipStream_t s,
-                   bool dry, const char** name, int forced) {
+int dispatch_typed(const GemmParams& p, bool fast, bool bt, bool at, bool big, bool k_slab,
+                   hipStream_t s, bool dry, const char** name, int forced) {
   // N-contiguous B: the two-group kernel's transpose-read form from 128 tiles
   // of 256 x 256 on, as in the fast layout, the 128 x 128 kernel below (bf16,
   // four alternating rounds, medians: 4096^3 with C, bias and ReLU 109.4
   // against 139.3 us, 8192^2 x 2048 213.7 against 283.5 us, 3072^2 x 4096,
   // 144 tiles, 79.9 against 91.9 us; 2048^3 38.8 against 20.1 us)
-  int v = forced >= 0 ? forced : ((fast || bt) ? (big ? 0 : 1) : 2);
-  // a fast variant needs the fast layout (variants 0 and 1 also take `bt`)
-  if (v != 2 && !fast && !(v <= 1 && bt)) return TLA_ERR_UNSUPPORTED;
+  // M-contiguous 16-bit A (`at`): variant 1's kernel at every size
+  int v = forced >= 0 ? forced : ((fast || bt) ? (big ? 0 : 1) : (at ? 1 : 2));
+  // a fast variant needs the fast layout (variants 0 and 1 also take `bt`,
+  // variant 1 `at`)
+  if (v != 2 && !fast && !(v <= 1 && bt) && !(v == 1 && at)) return TLA_ERR_UNSUPPORTED;
   // e4m3's 128 x 128 and 256 x 256 kernels copy whole 128-byte slabs with no
   // range check: K off the slab takes the two-group kernel or the general one
   if constexpr (kCode == kE4M3) {
@@ -390,6 +429,10 @@ int dispatch_typed(const GemmParams& p, bool fast, bool bt, bool big, bool k_sla
   if (name) *name = kVariantNames[v];
   if (dry) return TLA_OK;
   if constexpr (kCode != kE4M3) {
+    if (v == 1 && at) {
+      if (p.b_sk != 1) return launch_fast<kCode, 128, 128, 128, 3, 1, 2, 4, false, true, true>(p, s);
+      return launch_fast<kCode, 128, 128, 128, 3, 1, 2, 4, false, false, true>(p, s);
+    }
     if (v == 0 && !fast) return launch_pingpong(p, kCode, s, true);
     if (v == 1 && !fast) return launch_fast<kCode, 128, 128, 128, 3, 1, 2, 4, false, true>(p, s);
   }
@@ -592,15 +635,24 @@ int gemm_dispatch(const GemmProblem& g, hipStream_t stream, bool dry_run, const 
   const bool bt = !fast && nt && a_vec && b_rows16 && g.N % 8 == 0 &&
                   (int64_t)g.M * g.lda * eb < (int64_t(1) << 31) &&
                   (int64_t)g.K * g.ldb * eb < (int64_t(1) << 31) && k_ok;
+  // A a 16-bit column-major M x K matrix with 16-byte aligned columns, M a
+  // multiple of 8, below 2 GiB; B K-contiguous or N-contiguous as above
+  const bool b_any = (b_vec && (int64_t)g.N * g.ldb * eb < (int64_t(1) << 31)) ||
+                     (nt && b_rows16 && g.N % 8 == 0 &&
+                      (int64_t)g.K * g.ldb * eb < (int64_t(1) << 31));
+  const bool at = eb == 2 && g.a_order == TLA_COL_MAJOR && ((g.lda * eb) % 16) == 0 &&
+                  aligned(g.A, 16) && g.M % 8 == 0 &&
+                  (int64_t)g.K * g.lda * eb < (int64_t(1) << 31) && k_ok && b_any;
   const int64_t tiles256 = ((g.M + 255) / 256) * ((g.N + 255) / 256);
   const bool big = tiles256 >= 128;
   switch (g.a_type) {
     case TLA_BF16:
-      return dispatch_typed<kBF16>(p, fast, bt, big, k_slab, stream, dry_run, name, forced);
+      return dispatch_typed<kBF16>(p, fast, bt, at, big, k_slab, stream, dry_run, name, forced);
     case TLA_F16:
-      return dispatch_typed<kF16>(p, fast, bt, big, k_slab, stream, dry_run, name, forced);
+      return dispatch_typed<kF16>(p, fast, bt, at, big, k_slab, stream, dry_run, name, forced);
     case TLA_E4M3:
-      return dispatch_typed<kE4M3>(p, fast, false, big, k_slab, stream, dry_run, name, forced);
+      return dispatch_typed<kE4M3>(p, fast, false, false, big, k_slab, stream, dry_run, name,
+                                   forced);
     default: return TLA_ERR_UNSUPPORTED;
   }
 }
