@@ -126,8 +126,8 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  *                            four (2x2 waves of 64x128 each) that take turns
  *                            between MFMA-only and memory phases; direct
  *                            global->LDS copies; every operand type (16-bit
- *                            operands may also have an N-contiguous B, as
- *                            for variant 1)
+ *                            operands may also have an N-contiguous B or an
+ *                            M-contiguous A, as for variant 1)
  *   1 "gemm_fast_128x128"    128x128 tiles, direct copies (16-bit: 8
  *                            wavefronts of 64x32; e4m3: 4 of 64x64); for
  *                            16-bit operands B may also be N-contiguous
@@ -139,10 +139,9 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  *                            ragged K
  *   3 "gemm_fast_256x256"    256x256 tiles, one group (16-bit: 8 wavefronts
  *                            of 128x64; e4m3: 4 of 128x128), direct copies
- * tla_gemm_epilogue picks one from the problem: in the fast layout and in
- * the N-contiguous-B layout, variant 0 with at least 128 tiles of 256x256
- * and 1 otherwise; in the M-contiguous-A layout variant 1; variant 2
- * outside them;
+ * tla_gemm_epilogue picks one from the problem: in the fast layout, the
+ * N-contiguous-B and the M-contiguous-A layouts, variant 0 with at least
+ * 128 tiles of 256x256 and 1 otherwise; variant 2 outside them;
  * tla_gemm_run_variant runs the one asked for, with the same semantics and
  * tolerance, or returns TLA_ERR_UNSUPPORTED when a fast variant is asked
  * for a problem without the fast layout (both operands K-contiguous,
@@ -152,7 +151,7 @@ int tla_gemm_variant(const tla_gemm_args *args, char *buf, int32_t cap);
  * for e4m3 below 128 tiles with other K is variant 2) -- variants 0 and 1
  * also accept the N-contiguous-B layout (16-bit operands; A as in the fast
  * layout; B row-major with 16-byte aligned rows, N and K multiples of 8, B
- * below 2 GiB), and variant 1 the M-contiguous-A layout (16-bit operands; A
+ * below 2 GiB) and the M-contiguous-A layout (16-bit operands; A
  * column-major with 16-byte aligned columns, M and K multiples of 8, A
  * below 2 GiB; B in either of the layouts above).
  * Variant ids outside [0, TLA_GEMM_VARIANTS) are TLA_ERR_INVALID_ARG.

@@ -124,10 +124,11 @@ def test_gemm_variant_choice():
     big_k = dict(M=4096, N=4096, K=4000, lda=4096, ldb=4096, ldd=4096)
     assert _variant(_args(**big_k))[1] == "gemm_pingpong_256x256"
     # column-major 16-bit A with aligned columns, M a multiple of 8: the
-    # 128 x 128 kernel's transpose-read form at every size, either B layout
+    # transpose-read forms, by the fast layout's rule, either B layout
     at = dict(a_order=tla.COL_MAJOR, M=4096, N=4096, K=4096, lda=4096, ldb=4096, ldd=4096)
-    assert _variant(_args(**at))[1] == "gemm_fast_128x128"
-    assert _variant(_args(**dict(at, b_order=tla.ROW_MAJOR)))[1] == "gemm_fast_128x128"
+    assert _variant(_args(**at))[1] == "gemm_pingpong_256x256"
+    assert _variant(_args(**dict(at, b_order=tla.ROW_MAJOR)))[1] == "gemm_pingpong_256x256"
+    assert _variant(_args(**dict(at, M=1024, N=1024, lda=1024, ldd=1024)))[1] == "gemm_fast_128x128"
     assert _variant(_args(**dict(at, M=4092, ldd=4096)))[1] == "gemm_general_128x128"  # M % 8
     assert _variant(_args(**dict(at, lda=4100)))[1] == "gemm_general_128x128"  # column pitch
     assert _variant(_args(**dict(at, a_type=tla.E4M3, b_type=tla.E4M3)))[1] == "gemm_general_128x128"
@@ -261,10 +262,9 @@ def test_run_variant_argument_errors():
     # aligned N-contiguous B: the single-group 256 x 256 kernel has no such form
     nn = _args(b_order=tla.ROW_MAJOR, ldb=64)
     assert tla.lib().tla_gemm_run_variant(ctypes.byref(nn), 3, None) == tla.ERR_UNSUPPORTED
-    # column-major A: only variant 1 has the transpose-read form for A
+    # column-major A: the single-group 256 x 256 kernel has no such form
     at = _args(a_order=tla.COL_MAJOR)
-    for v in (0, 3):
-        assert tla.lib().tla_gemm_run_variant(ctypes.byref(at), v, None) == tla.ERR_UNSUPPORTED
+    assert tla.lib().tla_gemm_run_variant(ctypes.byref(at), 3, None) == tla.ERR_UNSUPPORTED
     # e4m3 with K off the 128-byte slab: the 128 x 128 and 256 x 256 kernels
     # copy whole slabs without a range check
     e4 = _args(a_type=tla.E4M3, b_type=tla.E4M3, K=80, lda=80, ldb=80)

@@ -303,6 +303,31 @@ def test_column_major_a_fast_kernel_bit_exact(M, N, K, a_type, b_order):
     assert np.array_equal(W.d_logical(case, D), want)
 
 
+@pytest.mark.parametrize("b_order", [W.ROW, W.COL])
+@pytest.mark.parametrize("M,N,K", [(296, 264, 200), (520, 776, 1000)])
+def test_column_major_a_two_group_kernel_bit_exact(M, N, K, b_order):
+    """The two-group kernel's k-rows-of-m form for a column-major A (forced;
+    the dispatch takes it from 128 tiles of 256 x 256)."""
+    case = W.GemmCase(name="acol_pp", M=M, N=N, K=K, a_type=W.BF16, b_type=W.BF16,
+                      d_type=W.BF16, a_order=W.COL, b_order=b_order, alpha=1.5, beta=0.5,
+                      act=W.ACT_RELU, has_c=True, has_bias=True, seed=M + N + K + 2,
+                      dist_a="int3", dist_b="int3", dist_c="int3", dist_bias="eighths")
+    case.lda += 8
+    case.ldb += 8 if b_order == W.COL else 16
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT[W.BF16], variant=0)
+    assert G.padding_untouched(case, D, SENT[W.BF16])
+    want = W.encode(G.oracle_ref(case, inp), W.BF16).reshape(M, N)
+    assert np.array_equal(W.d_logical(case, D), want)
+
+
+def test_column_major_a_random_4096_auto():
+    case = _small(M=4096, N=4096, K=1024, a_order=W.COL, b_order=W.ROW, act=W.ACT_RELU,
+                  seed=25)
+    assert G.variant(case) == "gemm_pingpong_256x256"
+    _check_sampled(case, W.gemm_inputs(case), seed=6)
+
+
 def test_column_major_a_fast_kernel_random_2048():
     case = _small(M=2048, N=2048, K=1024, a_order=W.COL, act=W.ACT_GELU, seed=24)
     assert G.variant(case) == "gemm_fast_128x128"

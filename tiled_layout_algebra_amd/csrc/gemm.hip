@@ -415,11 +415,11 @@ int dispatch_typed(const GemmParams& p, bool fast, bool bt, bool at, bool big, b
   // four alternating rounds, medians: 4096^3 with C, bias and ReLU 109.4
   // against 139.3 us, 8192^2 x 2048 213.7 against 283.5 us, 3072^2 x 4096,
   // 144 tiles, 79.9 against 91.9 us; 2048^3 38.8 against 20.1 us)
-  // M-contiguous 16-bit A (`at`): variant 1's kernel at every size
-  int v = forced >= 0 ? forced : ((fast || bt) ? (big ? 0 : 1) : (at ? 1 : 2));
-  // a fast variant needs the fast layout (variants 0 and 1 also take `bt`,
-  // variant 1 `at`)
-  if (v != 2 && !fast && !(v <= 1 && bt) && !(v == 1 && at)) return TLA_ERR_UNSUPPORTED;
+  // M-contiguous 16-bit A (`at`): the same rule
+  int v = forced >= 0 ? forced : ((fast || bt || at) ? (big ? 0 : 1) : 2);
+  // a fast variant needs the fast layout (variants 0 and 1 also take `bt`
+  // and `at`)
+  if (v != 2 && !fast && !(v <= 1 && (bt || at))) return TLA_ERR_UNSUPPORTED;
   // e4m3's 128 x 128 and 256 x 256 kernels copy whole 128-byte slabs with no
   // range check: K off the slab takes the two-group kernel or the general one
   if constexpr (kCode == kE4M3) {
@@ -429,6 +429,7 @@ int dispatch_typed(const GemmParams& p, bool fast, bool bt, bool at, bool big, b
   if (name) *name = kVariantNames[v];
   if (dry) return TLA_OK;
   if constexpr (kCode != kE4M3) {
+    if (v == 0 && at) return launch_pingpong(p, kCode, s, p.b_sk != 1, true);
     if (v == 1 && at) {
       if (p.b_sk != 1) return launch_fast<kCode, 128, 128, 128, 3, 1, 2, 4, false, true, true>(p, s);
       return launch_fast<kCode, 128, 128, 128, 3, 1, 2, 4, false, false, true>(p, s);

@@ -49,8 +49,10 @@ struct GemmParams {
 // operands in the fast layout (both operands K-contiguous with 16-byte
 // aligned rows, K a multiple of 16 bytes, each operand below 2 GiB); with
 // `bt`, 16-bit operands whose B is N-contiguous instead (16-byte aligned
-// rows, N a multiple of 8).
-int launch_pingpong(const GemmParams& p, int a_type, hipStream_t stream, bool bt = false);
+// rows, N a multiple of 8); with `at`, 16-bit operands whose A is
+// M-contiguous (16-byte aligned columns, M a multiple of 8).
+int launch_pingpong(const GemmParams& p, int a_type, hipStream_t stream, bool bt = false,
+                    bool at = false);
 const void* pingpong_kernel(int a_type);
 
 // The four-wavefront kernel of gemm_general.hip.  launch_general: its

@@ -50,7 +50,7 @@
 namespace tla {
 namespace {
 
-template <int kCode, bool kBT = false>
+template <int kCode, bool kBT = false, bool kAT = false>
 __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) {
   using Atom = MfmaAtom<kCode>;
   using Frag = typename Atom::Frag;
@@ -73,6 +73,7 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
                 "the swizzle repeats within 32 rows");
   static_assert(5 * SLAB <= 160 * 1024, "LDS budget");
   static_assert(!kBT || EB == 2, "N-contiguous B: 16-bit operands");
+  static_assert(!kAT || EB == 2, "M-contiguous A: 16-bit operands");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * SLAB];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -121,12 +122,29 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
       static_for<kCopies>([&](auto q) { recs[q] = (int)min(whole, (int64_t)0x7FFFFFFF); });
     }
   }
+  if constexpr (kAT) {
+    if (grp == 0) {
+      // the same for an M-contiguous A (column-major M x K, pitch lda):
+      // row rt (+ 8 q) of k, stored chunk t % 32 holding columns
+      // m0 + 8 ((t % 32) ^ 4 (rt % 4)) .. + 7, clamped to the last chunk of M
+      const int64_t lda = p.a_sk;
+      const int rt = t >> 5;
+      const int m = min(m0 + 8 * ((t & 31) ^ (4 * (rt & 3))), p.M - 8);
+      voff = (uint32_t)((rt * lda + m) * EB);
+      kt_bytes = (uint32_t)(BK * lda * EB);
+      q_bytes = (uint32_t)(8 * lda * EB);
+      qbase = p.A;
+      q_stride = 0;
+      const int64_t whole = (int64_t)p.K * lda * EB;
+      static_for<kCopies>([&](auto q) { recs[q] = (int)min(whole, (int64_t)0x7FFFFFFF); });
+    }
+  }
   // The ragged last k-tile (K a multiple of the 16-byte chunk): a lane whose
   // K-contiguous chunk lies past K reads from past every record, so the
-  // range check returns zeros; an N-contiguous B slab's rows past K are
-  // past its records already.
+  // range check returns zeros; the rows past K of a k-rows slab (an M- or
+  // N-contiguous operand) are past its records already.
   uint32_t voff_tail = voff;
-  if (grp == 0 || !kBT) {
+  if ((grp == 0 && !kAT) || (grp == 1 && !kBT)) {
     if (Swz::chunk(r0, t % kChunks) * 16 >= (p.K - KTf * BK) * EB) voff_tail = 0x80000000u;
   }
   // Copy q of k-tile kt into `slot`.  A copy past the last k-tile still runs
@@ -152,14 +170,22 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   // one's address XOR 16 (every other term of the address is a multiple of
   // 128), formed in the loop rather than held.
   static_assert(kSub == 1 || (Atom::kLaneBytes == 32 && kStepBytes % 32 == 0), "chunk pairs");
-  uint32_t fa[KSTEPS], fb[kBT ? 1 : KSTEPS];
+  uint32_t fa[kAT ? 1 : KSTEPS], fb[kBT ? 1 : KSTEPS];
   static_for<KSTEPS>([&](auto ks) {
     const int c = (ks * kStepBytes + (lane >> 5) * Atom::kLaneBytes) / 16;
     const int ra = wm0 + (lane & 31), rbw = wn0 + (lane & 31);
-    fa[ks] = (uint32_t)(ra * kRowBytes + Swz::chunk(ra, c) * 16);
+    if constexpr (!kAT) fa[ks] = (uint32_t)(ra * kRowBytes + Swz::chunk(ra, c) * 16);
     if constexpr (!kBT)
       fb[ks] = (uint32_t)(B_BASE + rbw * kRowBytes + Swz::chunk(rbw, c) * 16);  // B slot 0
   });
+  if constexpr (kAT) {
+    // as for an N-contiguous B below, with rows m = wm0 + ... of A slot 0
+    // (wm0 is a multiple of 64, so fragment i is again XOR 64 i)
+    const int qw = lane >> 4, a4 = lane & 15;
+    const int k = 8 * (qw >> 1) + (a4 >> 2);
+    const int m = wm0 + 16 * (qw & 1) + 4 * (a4 & 3);
+    fa[0] = (uint32_t)(k * 512 + (((m >> 3) ^ (4 * (k & 3))) * 16) + (m & 7) * 2);
+  }
   if constexpr (kBT) {
     // transpose read h of k-step ks for lane a of quarter-wave qw: row
     // k = 16 ks + 8 (qw / 2) + 4 h + a / 4, columns n = wn0 + 16 (qw % 2) +
@@ -195,7 +221,9 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   };
   auto read_frag = [&](int kt, auto r) {
     constexpr int ks = r / (FM + FN), f = r % (FM + FN);
-    if constexpr (f < FM)
+    if constexpr (f < FM && kAT)
+      a[ks][f] = lds_frag_t((fa[0] ^ (64u * f)) + 8192 * ks + (kt & 1) * SLAB);
+    else if constexpr (f < FM)
       a[ks][f] = lds_frag(fa[ks], (kt & 1) * SLAB + f * 32 * kRowBytes);
     else if constexpr (kBT)
       b[ks][f - FM] = lds_frag_t((fb[0] ^ (64u * (f - FM))) + 8192 * ks);
@@ -220,7 +248,8 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
   // LDS read instructions of fragments [first, first + n)
   auto read_insts = [](int first, int n) constexpr {
     int c = 0;
-    for (int r = first; r < first + n; ++r) c += (r % (FM + FN) < FM || !kBT) ? kSub : 2;
+    for (int r = first; r < first + n; ++r)
+      c += (r % (FM + FN) < FM) ? (kAT ? 2 : kSub) : (kBT ? 2 : kSub);
     return c;
   };
   auto memory_phase = [&](int kt, int ct, int slot, bool live) {
@@ -326,12 +355,29 @@ __global__ __launch_bounds__(512) void gemm_pingpong_kernel(const GemmParams p) 
 
 }  // namespace
 
-int launch_pingpong(const GemmParams& p0, int a_type, hipStream_t stream, bool bt) {
+int launch_pingpong(const GemmParams& p0, int a_type, hipStream_t stream, bool bt, bool at) {
   GemmParams p = p0;
   int64_t grid;
   set_grid(p, 256, 256, &grid);
   if (grid <= 0) return TLA_OK;
   if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
+  if (at) {
+    if (a_type == kBF16 && bt)
+      hipLaunchKernelGGL((gemm_pingpong_kernel<kBF16, true, true>), dim3((unsigned)grid),
+                         dim3(512), 0, stream, p);
+    else if (a_type == kBF16)
+      hipLaunchKernelGGL((gemm_pingpong_kernel<kBF16, false, true>), dim3((unsigned)grid),
+                         dim3(512), 0, stream, p);
+    else if (a_type == kF16 && bt)
+      hipLaunchKernelGGL((gemm_pingpong_kernel<kF16, true, true>), dim3((unsigned)grid),
+                         dim3(512), 0, stream, p);
+    else if (a_type == kF16)
+      hipLaunchKernelGGL((gemm_pingpong_kernel<kF16, false, true>), dim3((unsigned)grid),
+                         dim3(512), 0, stream, p);
+    else
+      return TLA_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
+  }
   if (bt) {
     if (a_type == kBF16)
       hipLaunchKernelGGL((gemm_pingpong_kernel<kBF16, true>), dim3((unsigned)grid), dim3(512), 0,
