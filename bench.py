@@ -22,6 +22,7 @@ unit-stride runs on both sides) are timed on their own.
     python bench.py --variants [--steps K] [--warmup W]  # big GEMMs, each fast variant
 """
 import argparse
+import itertools
 import json
 import os
 import sys
@@ -115,12 +116,15 @@ def sweep(steps, warmup):
                                  "←" if info["name"] == auto else ""))
                 print(lines[-1], file=sys.stderr, flush=True)
             del dA, dB, dD
-    # bf16 with a row-major (N-contiguous) B: the variants that accept it
-    lines += ["", "| B row-major (bf16) | variant | M×N×K | µs | TFLOP/s | % peak | auto |",
+    # bf16 with a row-major (N-contiguous) B or a column-major (M-contiguous)
+    # A: the variants that accept them
+    lines += ["", "| operand layouts (bf16) | variant | M×N×K | µs | TFLOP/s | % peak | auto |",
               "|---|---|---|---|---|---|---|"]
-    for M, N, K in SWEEP_SHAPES:
+    layouts = ((W.ROW, W.ROW, "bf16 NN"), (W.COL, W.COL, "bf16 A col, B col"),
+               (W.COL, W.ROW, "bf16 A col, B row"))
+    for (a_order, b_order, label), (M, N, K) in itertools.product(layouts, SWEEP_SHAPES):
         case = W.GemmCase(name="sweep_nn", M=M, N=N, K=K, a_type=W.BF16, b_type=W.BF16,
-                          d_type=W.BF16, b_order=W.ROW, seed=7)
+                          d_type=W.BF16, a_order=a_order, b_order=b_order, seed=7)
         inp = W.gemm_inputs(case)
         dA, dB = to_dev(inp["A"]), to_dev(inp["B"])
         dD = torch.empty(M * N, dtype=torch.int16, device="cuda")
@@ -142,8 +146,8 @@ def sweep(steps, warmup):
             us = e0.elapsed_time(e1) * 1e3 / steps
             tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
             name = tla.gemm_variant_info(v, W.BF16)["name"]
-            lines.append("| bf16 NN | %s | %d×%d×%d | %.1f | %.0f | %.1f | %s |" % (
-                name, M, N, K, us, tf, 100 * tf / PEAK_BF16_TFLOPS, "←" if name == auto else ""))
+            lines.append("| %s | %s | %d×%d×%d | %.1f | %.0f | %.1f | %s |" % (
+                label, name, M, N, K, us, tf, 100 * tf / PEAK_BF16_TFLOPS, "←" if name == auto else ""))
             print(lines[-1], file=sys.stderr, flush=True)
         del dA, dB, dD
     # pitches off 16-byte alignment (every leading dimension one element past
