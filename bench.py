@@ -116,22 +116,26 @@ def sweep(steps, warmup):
                                  "←" if info["name"] == auto else ""))
                 print(lines[-1], file=sys.stderr, flush=True)
             del dA, dB, dD
-    # bf16 with a row-major (N-contiguous) B or a column-major (M-contiguous)
-    # A: the variants that accept them
-    lines += ["", "| operand layouts (bf16) | variant | M×N×K | µs | TFLOP/s | % peak | auto |",
+    # a row-major (N-contiguous) B or a column-major (M-contiguous) A: the
+    # variants that accept them (e4m3: the general kernel only)
+    lines += ["", "| operand layouts | variant | M×N×K | µs | TFLOP/s | % peak | auto |",
               "|---|---|---|---|---|---|---|"]
-    layouts = ((W.ROW, W.ROW, "bf16 NN"), (W.COL, W.COL, "bf16 A col, B col"),
-               (W.COL, W.ROW, "bf16 A col, B row"))
-    for (a_order, b_order, label), (M, N, K) in itertools.product(layouts, SWEEP_SHAPES):
-        case = W.GemmCase(name="sweep_nn", M=M, N=N, K=K, a_type=W.BF16, b_type=W.BF16,
+    layouts = ((W.BF16, W.ROW, W.ROW, "bf16 NN", (0, 1, 2)),
+               (W.BF16, W.COL, W.COL, "bf16 A col, B col", (0, 1, 2)),
+               (W.BF16, W.COL, W.ROW, "bf16 A col, B row", (0, 1, 2)),
+               (W.E4M3, W.ROW, W.ROW, "e4m3 NN", (2,)),
+               (W.E4M3, W.COL, W.COL, "e4m3 A col, B col", (2,)))
+    for (a_type, a_order, b_order, label, variants), (M, N, K) in itertools.product(
+            layouts, SWEEP_SHAPES):
+        case = W.GemmCase(name="sweep_nn", M=M, N=N, K=K, a_type=a_type, b_type=a_type,
                           d_type=W.BF16, a_order=a_order, b_order=b_order, seed=7)
         inp = W.gemm_inputs(case)
         dA, dB = to_dev(inp["A"]), to_dev(inp["B"])
         dD = torch.empty(M * N, dtype=torch.int16, device="cuda")
-        call = (M, N, K, dA, W.BF16, case.a_order, case.lda, dB, W.BF16, case.b_order,
+        call = (M, N, K, dA, a_type, case.a_order, case.lda, dB, a_type, case.b_order,
                 case.ldb, dD, W.BF16, case.d_order, case.ldd)
         auto = tla.gemm_variant(*call)
-        for v in (0, 1, 2):
+        for v in variants:
             def run():
                 tla.gemm_epilogue(*call, stream=stream.cuda_stream, variant=v)
             for _ in range(warmup):
@@ -145,9 +149,9 @@ def sweep(steps, warmup):
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / steps
             tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
-            name = tla.gemm_variant_info(v, W.BF16)["name"]
+            name = tla.gemm_variant_info(v, a_type)["name"]
             lines.append("| %s | %s | %d×%d×%d | %.1f | %.0f | %.1f | %s |" % (
-                label, name, M, N, K, us, tf, 100 * tf / PEAK_BF16_TFLOPS, "←" if name == auto else ""))
+                label, name, M, N, K, us, tf, 100 * tf / peaks[a_type], "←" if name == auto else ""))
             print(lines[-1], file=sys.stderr, flush=True)
         del dA, dB, dD
     # pitches off 16-byte alignment (every leading dimension one element past

@@ -280,6 +280,31 @@ def test_column_major_a_bit_exact(M, N, K, a_type, b_order):
     assert np.array_equal(W.d_logical(case, D), want)
 
 
+@pytest.mark.parametrize("a_order,b_order", [(W.COL, W.COL), (W.ROW, W.ROW), (W.COL, W.ROW)])
+@pytest.mark.parametrize("M,N,K,pad", [(300, 264, 200, 16), (7, 40, 131, 0), (1031, 257, 777, 32),
+                                       (1024, 1024, 1024, 0)])
+def test_e4m3_runs_along_m_or_n_bit_exact(M, N, K, pad, a_order, b_order):
+    """e4m3 with A column-major and/or B row-major, every run along M or N
+    16-byte aligned (pitch: the extent rounded up to 16, plus pad): the
+    general kernel loads those runs whole and transposes them in registers
+    into its rows-of-k slab.  Ragged M, N and K cross the tile edges, the
+    pitch padding holds NaN; integer inputs, so D is exact."""
+    case = W.GemmCase(name="e4runs", M=M, N=N, K=K, a_type=W.E4M3, b_type=W.E4M3,
+                      d_type=W.BF16, a_order=a_order, b_order=b_order, alpha=1.5, beta=0.5,
+                      act=W.ACT_RELU, has_c=True, has_bias=True, seed=M + N + K + pad,
+                      dist_a="int3", dist_b="int3", dist_c="int3", dist_bias="eighths")
+    if a_order == W.COL:
+        case.lda = -(-M // 16) * 16 + pad
+    if b_order == W.ROW:
+        case.ldb = -(-N // 16) * 16 + pad
+    assert G.variant(case) == "gemm_general_128x128"
+    inp = W.gemm_inputs(case)
+    D = G.run_gemm(case, inp, sentinel=SENT[W.BF16])
+    assert G.padding_untouched(case, D, SENT[W.BF16])
+    want = W.encode(G.oracle_ref(case, inp), W.BF16).reshape(M, N)
+    assert np.array_equal(W.d_logical(case, D), want)
+
+
 @pytest.mark.parametrize("b_order", [W.ROW, W.COL])
 @pytest.mark.parametrize("a_type", [W.F16, W.BF16])
 @pytest.mark.parametrize("M,N,K", [(296, 264, 200), (8, 40, 64), (1024, 520, 1000)])

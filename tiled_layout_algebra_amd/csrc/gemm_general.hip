@@ -32,15 +32,76 @@ namespace {
 // (RegSlabNT), e4m3 A goes through element loads; kBView: B K-contiguous
 // (kBK), N-contiguous through element loads (kBN), or N-contiguous 16-bit
 // with its slab as k rows of n (RegSlabNT, kBNT).  A k-rows slab is read
-// into fragments by transposing LDS reads.
+// into fragments by transposing LDS reads.  kT8: an e4m3 operand that is M-
+// or N-contiguous with 16-byte aligned runs is loaded by RegSlabT8 instead
+// of element loads.
 enum : int { kBK = 0, kBN = 1, kBNT = 2 };
+
+// An 8-bit operand stored with its rows of m (or n) contiguous -- a column-
+// major A or a row-major B -- whose runs are 16-byte aligned.  Thread t
+// loads the 16-byte runs of rows 16 (t % 8) .. + 15 at the four k indices
+// 4 (t / 8) .. + 3, transposes the 4 x 16 bytes in registers and writes 16
+// dwords of four consecutive k each, so the slab holds the tile as rows of
+// k (swizzled 16-byte chunks), as the K-contiguous loader leaves it, and the
+// fragment reads do not change.  One 128-row by 128-byte tile per 256
+// threads.  Indices k past K load as zero and so do rows past the edge; the
+// run that crosses the edge is gathered byte by byte, clamped in bounds.
+template <int ROWS, int kRowBytes>
+struct RegSlabT8 {
+  using Swz = typename Slab<kRowBytes>::Swz;
+  static_assert(ROWS == 128 && kRowBytes == 128 && kThreads == 256,
+                "128 x 128-byte tile on 256 threads");
+  i32x4 v[4];
+
+  // k0 .. k0 + 127 inside K, rows row0 .. row0 + 127 inside rows_valid;
+  // s: the k stride in elements (a multiple of 16, base 16-byte aligned)
+  __device__ __forceinline__ void load_whole(const uint8_t* __restrict__ base, int64_t s, int row0,
+                                             int rows_valid, int k0, int tid) {
+    const uint8_t* q = base + (int64_t)(k0 + 4 * (tid >> 3)) * s + row0 + 16 * (tid & 7);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) v[it] = *(const i32x4*)(q + it * s);
+  }
+
+  __device__ __forceinline__ void load_edge(const uint8_t* __restrict__ base, int64_t s, int row0,
+                                            int rows_valid, int k0, int K, int tid) {
+    const int c = row0 + 16 * (tid & 7);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int k = k0 + 4 * (tid >> 3) + it;
+      i32x4 x = {0, 0, 0, 0};
+      if (k < K && c < rows_valid) {
+        const uint8_t* row = base + (int64_t)k * s;
+        if (c + 16 <= rows_valid)
+          x = *(const i32x4*)(row + c);
+        else
+          x = gather16<1>(row, 1, c, rows_valid, rows_valid - 1);
+      }
+      v[it] = x;
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* slab, int tid) const {
+    const int kk = 4 * (tid >> 3), r0 = 16 * (tid & 7);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t x0 = v[0][d], x1 = v[1][d], x2 = v[2][d], x3 = v[3][d];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t y = ((x0 >> (8 * b)) & 0xffu) | (((x1 >> (8 * b)) & 0xffu) << 8) |
+                           (((x2 >> (8 * b)) & 0xffu) << 16) | (((x3 >> (8 * b)) & 0xffu) << 24);
+        const int r = r0 + 4 * d + b;
+        *(uint32_t*)(slab + r * kRowBytes + Swz::chunk(r, kk >> 4) * 16 + (kk & 15)) = y;
+      }
+    }
+  }
+};
 
 // The register-staged form without element-wise views asks for two waves
 // per SIMD (at most 256 VGPRs): left to itself the compiler let its two
 // register sets push the kernel to 260-316 VGPRs, one wave per SIMD.  With
 // an element-wise view it would spill, so those keep one.
 template <int kCode, int BM, int BN, int kRowBytes, int kStages, bool kFast, bool kConv = false,
-          bool kAKC = true, int kBView = kBK>
+          bool kAKC = true, int kBView = kBK, bool kT8 = false>
 __global__ __launch_bounds__(kThreads, (kFast || (!kAKC && elem_bytes(kCode) != 2) ||
                                         kBView == kBN) ? 1 : 2) void gemm_kernel(const GemmParams p) {
   constexpr bool kNT = kBView == kBNT;
@@ -58,6 +119,9 @@ __global__ __launch_bounds__(kThreads, (kFast || (!kAKC && elem_bytes(kCode) != 
   static_assert(!kNT || (EB == 2 && Atom::kK == 16 && !kFast && !kConv),
                 "N-contiguous B slab: 16-bit operands, register-staged path");
   static_assert(!(kFast || kConv) || (kAKC && kBView == kBK), "K-contiguous operands");
+  static_assert(!kT8 || (EB == 1 && BM == 128 && BN == 128 && kRowBytes == 128 && !kFast &&
+                         (!kAKC || kBView == kBN)), "8-bit runs along M or N");
+  constexpr bool kA8 = kT8 && !kAKC, kB8 = kT8 && kBView == kBN;
   // global_load_lds instructions one thread issues per k-tile
   constexpr int kLoadsPerTile = (BM + BN) * kRowBytes / 16 / kThreads;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * STAGE];
@@ -179,8 +243,12 @@ __global__ __launch_bounds__(kThreads, (kFast || (!kAKC && elem_bytes(kCode) != 
     // ahead through the edge loader.  Tile t lives in LDS stage t % 2.
     using RA = std::conditional_t<
         kConv, ConvSlab<BM, EB, kRowBytes>,
-        std::conditional_t<kAT, RegSlabNT<BM, BK>, RegSlab<BM, EB, kRowBytes, kAKC>>>;
-    using RB = std::conditional_t<kNT, RegSlabNT<BN, BK>, RegSlab<BN, EB, kRowBytes, kBView == kBK>>;
+        std::conditional_t<kAT, RegSlabNT<BM, BK>,
+                           std::conditional_t<kA8, RegSlabT8<BM, kRowBytes>,
+                                              RegSlab<BM, EB, kRowBytes, kAKC>>>>;
+    using RB = std::conditional_t<
+        kNT, RegSlabNT<BN, BK>,
+        std::conditional_t<kB8, RegSlabT8<BN, kRowBytes>, RegSlab<BN, EB, kRowBytes, kBView == kBK>>>;
     RA ra[2];
     RB rb[2];
     const bool a_vec = (p.flags >> 8) & 1;
@@ -190,7 +258,7 @@ __global__ __launch_bounds__(kThreads, (kFast || (!kAKC && elem_bytes(kCode) != 
       if constexpr (kConv) {
         ra[set].load_conv(p, m0, k0, a_vec, tid);
       } else {
-        if constexpr (kAT) {
+        if constexpr (kAT || kA8) {
           if constexpr (whole) ra[set].load_whole(p.A, a_s, m0, p.M, k0, tid);
           else ra[set].load_edge(p.A, a_s, m0, p.M, k0, p.K, tid);
         } else {
@@ -198,7 +266,7 @@ __global__ __launch_bounds__(kThreads, (kFast || (!kAKC && elem_bytes(kCode) != 
           else ra[set].load_edge(p.A, a_s, m0, p.M, k0, p.K, tid);
         }
       }
-      if constexpr (kNT) {
+      if constexpr (kNT || kB8) {
         if constexpr (whole) rb[set].load_whole(p.B, b_s, n0, p.N, k0, tid);
         else rb[set].load_edge(p.B, b_s, n0, p.N, k0, p.K, tid);
       } else {
@@ -217,7 +285,11 @@ __global__ __launch_bounds__(kThreads, (kFast || (!kAKC && elem_bytes(kCode) != 
     // whole tiles: inside K; for a k-rows slab of a tile that crosses M or N
     // also before the tile holding row K - 1 (its chunks read past the edge)
     const bool m_edge = kAT && m0 + BM > p.M, n_edge = kNT && n0 + BN > p.N;
-    const int KTw = (m_edge || n_edge)
+    // (the 8-bit runs loader has no clamped whole load: its edge tiles take
+    // the edge loop throughout)
+    const bool t8_edge = (kA8 && m0 + BM > p.M) || (kB8 && n0 + BN > p.N);
+    const int KTw = t8_edge ? 0
+                    : (m_edge || n_edge)
                         ? ((m_edge && p.M < 8) || (n_edge && p.N < 8) ? 0 : (p.K - 1) / BK)
                         : p.K / BK;
     if (KT > 0) {
@@ -275,14 +347,15 @@ __global__ __launch_bounds__(kThreads, (kFast || (!kAKC && elem_bytes(kCode) != 
 }
 
 
-template <int kCode, int BM, int BN, bool kFast, bool kConv, bool kAKC, int kBView>
+template <int kCode, int BM, int BN, bool kFast, bool kConv, bool kAKC, int kBView,
+          bool kT8 = false>
 int launch(const GemmParams& p0, hipStream_t stream) {
   GemmParams p = p0;
   int64_t grid;
   set_grid(p, BM, BN, &grid);
   if (grid <= 0) return TLA_OK;
   if (grid > 0x7FFFFFFF) return TLA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((gemm_kernel<kCode, BM, BN, 128, 2, kFast, kConv, kAKC, kBView>),
+  hipLaunchKernelGGL((gemm_kernel<kCode, BM, BN, 128, 2, kFast, kConv, kAKC, kBView, kT8>),
                      dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TLA_OK : TLA_ERR_HIP;
 }
@@ -297,6 +370,18 @@ template <int kCode>
 int launch_views(const GemmParams& p, hipStream_t s) {
   constexpr int kBNc = kCode == kE4M3 ? kBN : kBNT;
   const bool akc = p.a_sk == 1, bkc = p.b_sk == 1;
+  if constexpr (kCode == kE4M3) {
+    // M- or N-contiguous e4m3 operands with 16-byte aligned runs: RegSlabT8
+    // (4096^3 with both operands column-major: 1130 us with element loads)
+    auto runs16 = [](const void* q, int64_t ld) {
+      return (reinterpret_cast<uintptr_t>(q) & 15) == 0 && ld % 16 == 0;
+    };
+    if ((!akc || !bkc) && (akc || runs16(p.A, p.a_sk)) && (bkc || runs16(p.B, p.b_sk))) {
+      if (akc) return launch<kCode, 128, 128, false, false, true, kBN, true>(p, s);
+      return bkc ? launch<kCode, 128, 128, false, false, false, kBK, true>(p, s)
+                 : launch<kCode, 128, 128, false, false, false, kBN, true>(p, s);
+    }
+  }
   if (akc)
     return bkc ? launch<kCode, 128, 128, false, false, true, kBK>(p, s)
                : launch<kCode, 128, 128, false, false, true, kBNc>(p, s);
